@@ -1,0 +1,408 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these checks re-types an oracle formula: each compares against a value
+the pages print (tests/golden, cited there), a closed form, an invariant, a
+library routine, or brute force on tiny inputs.  Every check is chosen so that
+a plausible slip (a swapped exponent, a multiply for a divide, a transposed
+operand, a wrong scale axis, round-half-away, a -128 clamp) fails it.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    vals, cases = {}, []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = [t.strip() for t in line.split("=", 1)]
+            if k == "case":
+                cases.append(v)
+            else:
+                vals[k] = float(v)
+    return vals, cases
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+def ulp(x):
+    x = np.abs(f32(x))
+    return np.spacing(x)
+
+
+# ---- eq. (3) direction and the worked examples --------------------------------
+
+def test_worked_example_s10():
+    """[Teach] §三: peaks 120 / 0.12 with s = 10 become 12 / 1.2, product kept."""
+    g, _ = _golden("worked_example_s10.txt")
+    x = f32([[g["act_peak"]], [-0.5 * g["act_peak"]]])        # 2 tokens, 1 channel
+    w = f32([[g["weight_peak"]], [-0.25 * g["weight_peak"]]])  # 2 outputs, 1 channel
+    s = f32([g["s"]])
+    xhat = oracle.act_smooth(x, s)
+    assert np.abs(xhat).max() == np.float32(g["smoothed_act_peak"])
+    # the smoothed weight peak is recovered from the row-0 scale: 127 * d_0 = peak
+    wq, wsc = oracle.weight_quant(w, s)
+    assert wq[0, 0] == 127
+    assert abs(float(wsc[0]) * 127.0 - g["smoothed_weight_peak"]) <= 2 * float(ulp(1.2))
+    # the LayerNorm fold divides gamma and beta (activation side of the rewrite)
+    gs, bs = oracle.ln_fold(f32([g["act_peak"]]), f32([g["act_peak"]]), s)
+    assert gs[0] == np.float32(g["smoothed_act_peak"]) and bs[0] == gs[0]
+    # products unchanged in fp64 (eq. (3))
+    y = oracle.ref_linear_f64(x, w)
+    yh = oracle.ref_smoothed_linear_f64(x, w, s)
+    np.testing.assert_allclose(yh, y, rtol=1e-12, atol=0)
+    assert abs(y[0, 0] - g["product"]) < 1e-5
+
+
+def test_toy_example_s50():
+    """[Review] §5.4: channel 1 at 100, others 1..3; /50 on X and *50 on W."""
+    g, _ = _golden("toy_example_s50.txt")
+    rng = np.random.default_rng(7)
+    K = 8
+    x = rng.uniform(g["other_lo"], g["other_hi"], size=(16, K)).astype(np.float32)
+    x[3, 1] = g["outlier_peak"]
+    s = np.ones(K, np.float32)
+    s[1] = g["s_outlier"]
+    xhat = oracle.act_smooth(x, s)
+    assert np.abs(xhat[:, 1]).max() == np.float32(g["smoothed_outlier_peak"])
+    # other channels untouched (s = 1 is an exact identity)
+    np.testing.assert_array_equal(xhat[:, [0, 2, 3, 4, 5, 6, 7]], x[:, [0, 2, 3, 4, 5, 6, 7]])
+    w = rng.normal(0, 0.02, size=(5, K)).astype(np.float32)
+    np.testing.assert_allclose(oracle.ref_smoothed_linear_f64(x, w, s),
+                               oracle.ref_linear_f64(x, w), rtol=1e-12, atol=1e-15)
+
+
+# ---- eq. (4) -------------------------------------------------------------------
+
+def test_alpha_half_closed_form():
+    """Eq. (4) at alpha = 0.5 reduces to sqrt(a / w) (golden, derived by hand)."""
+    g, _ = _golden("alpha_half_example.txt")
+    s = oracle.smooth_factor(f32([120.0]), f32([0.12]), g["alpha"])
+    assert abs(float(s[0]) / g["s"] - 1) < 1e-7
+    xhat_peak = np.float32(120.0) / s[0]
+    w_peak = np.float32(0.12) * s[0]
+    assert abs(float(xhat_peak) / g["smoothed_peak"] - 1) < 1e-6
+    assert abs(float(w_peak) / g["smoothed_peak"] - 1) < 1e-6
+
+
+@pytest.mark.parametrize("alpha", datagen.ALPHA_SWEEP + (0.1, 0.6, 0.9))
+def test_eq4_product_forms(alpha):
+    """a/s = (a w)^(1-alpha) and w s = (a w)^alpha: a swapped exponent, an
+    inverted ratio or a missing power fails this for alpha != 0.5."""
+    rng = np.random.default_rng(11)
+    a = rng.uniform(0.05, 120.0, 4096).astype(np.float32)
+    w = rng.uniform(1e-3, 0.2, 4096).astype(np.float32)
+    s = oracle.smooth_factor(a, w, alpha).astype(np.float64)
+    al = float(np.float32(alpha))  # the call takes alpha as fp32
+    aw = a.astype(np.float64) * w.astype(np.float64)
+    # fp32 rounding of s: relative error <= 2^-24
+    np.testing.assert_allclose(a / s, aw ** (1 - al), rtol=2 ** -23)
+    np.testing.assert_allclose(w * s, aw ** al, rtol=2 ** -23)
+
+
+def test_alpha_one_flattens_activation_channels():
+    """[Edge] §一.2 and [Review] §5.3: alpha = 1 puts every smoothed activation
+    channel peak at exactly 1 (exact under the division reading)."""
+    spec = datagen.workload(1).layers[0]
+    xc = datagen.calibration_x(spec)
+    w = datagen.weights(spec)
+    a, wm = oracle.colmax(xc), oracle.colmax(w)
+    s = oracle.smooth_factor(a, wm, 1.0)
+    np.testing.assert_array_equal(s, a)
+    peaks = oracle.colmax(oracle.act_smooth(xc, s))
+    np.testing.assert_array_equal(peaks, np.ones_like(peaks))
+    assert oracle.static_scale(a, s) == np.float32(1.0) / np.float32(127.0)
+
+
+def test_alpha_zero_normalises_weight_channels():
+    """Eq. (4) at alpha = 0: s = 1/w, so every smoothed weight channel peak is 1."""
+    rng = np.random.default_rng(3)
+    a = rng.uniform(0.1, 100, 2048).astype(np.float32)
+    w = rng.uniform(1e-4, 0.5, 2048).astype(np.float32)
+    s = oracle.smooth_factor(a, w, 0.0)
+    prod = w * s
+    assert np.all(np.abs(prod - 1) <= np.spacing(np.float32(1.0)))
+
+
+@pytest.mark.parametrize("alpha", datagen.ALPHA_SWEEP)
+def test_smooth_factor_quad_audit(alpha):
+    """fp64 pow/pow/divide rounds to the same fp32 as a quad-precision route;
+    no channel of a workload-shaped vector sits near an fp32 rounding tie."""
+    spec = datagen.workload(2).layers[0]
+    a = oracle.colmax(datagen.calibration_x(spec))
+    rng = np.random.default_rng(5)
+    w = rng.uniform(0.05, 0.1, spec.K).astype(np.float32)
+    near, mism = oracle.smooth_factor_audit(a, w, alpha)
+    assert mism == 0 and near == 0
+
+
+def test_colmax_matches_library_max():
+    x = datagen.calibration_x(datagen.workload(2).layers[1])
+    ref = np.maximum(np.abs(datagen.bf16_bits_to_f32(x)).max(axis=0), oracle.FLOOR)
+    np.testing.assert_array_equal(oracle.colmax(x), ref)
+    z = np.zeros((3, 64), np.float32)
+    np.testing.assert_array_equal(oracle.colmax(z), np.full(64, oracle.FLOOR, np.float32))
+
+
+# ---- quantizer ([Review] §2.2) ---------------------------------------------------
+
+def test_quantizer_ties_round_to_even_and_bound():
+    d = 1.0  # row peak 127 gives a step of exactly 1
+    row = f32([127.0, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, -1.5, 2.4999998, -126.5])
+    q, sc = oracle.quant_per_token(row[None, :])
+    assert sc[0] == np.float32(d)
+    np.testing.assert_array_equal(q[0], [127, 2, 4, -2, 0, 2, 0, -2, 2, -126])
+
+
+def test_quantizer_error_bound_and_symmetric_clamp():
+    rng = np.random.default_rng(9)
+    x = rng.normal(0, 1, size=(64, 1024)).astype(np.float32)
+    x[:, 17] *= 60
+    q, sc = oracle.quant_per_token(x)
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * sc[:, None].astype(np.float64))
+    assert np.all(err <= sc[:, None].astype(np.float64) / 2 * (1 + 1e-6))
+    assert q.min() >= -127 and q.max() <= 127
+    # every row uses the full code range (its peak maps to +-127)
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    # static scale: out-of-range values saturate at +-127 (never -128)
+    qs, sat = oracle.quant_static(f32([[300.0, -300.0, 127.4, -127.6, 0.2]]), np.float32(1.0))
+    np.testing.assert_array_equal(qs[0], [127, -127, 127, -127, 0])
+    assert sat == 3
+
+
+def test_effective_levels():
+    """[Review] §2.4: a channel with peak m_i in a tensor with peak m gets about
+    2^8 m_i/m levels.  Exact count for a densely filled channel:
+    2*rne(127 m_i/m) + 1 (the estimate 256 m_i/m counts 2^8 levels where the
+    symmetric quantizer has 255)."""
+    _, cases = _golden("effective_levels.txt")
+    for c in cases:
+        mi, m, est = (float(t) for t in c.split(","))
+        assert abs(est - 256 * mi / m) < 1e-9
+        ch = np.linspace(-mi, mi, 200001, dtype=np.float32)
+        x = np.zeros((2, ch.size), np.float32)
+        x[0] = ch
+        x[1, 0] = m
+        scale = np.float32(m) / np.float32(127)
+        q, _ = oracle.quant_static(x, scale)
+        levels = np.unique(q[0]).size
+        assert levels == 2 * round(127 * mi / m) + 1
+        # 2*rne(127 r)+1 vs 256 r: rounding adds at most one code per side
+        assert abs(levels - est) <= est * 2 / 256 + 2 + 1e-9
+
+
+# ---- weights: per-output-channel axis -----------------------------------------------
+
+def test_weight_scale_is_per_output_channel():
+    rng = np.random.default_rng(21)
+    N, K = 6, 256
+    w = rng.normal(0, 0.02, size=(N, K)).astype(np.float32)
+    w[2] *= 50.0                      # one loud output row
+    s = rng.uniform(0.5, 2.0, K).astype(np.float32)
+    wq, sc = oracle.weight_quant(w, s)
+    # each row reaches +-127 at its own peak
+    assert np.all(np.abs(wq).max(axis=1) == 127)
+    ws = w.astype(np.float64) * s.astype(np.float64)
+    np.testing.assert_allclose(sc.astype(np.float64) * 127, np.abs(ws).max(axis=1), rtol=1e-6)
+    # dequantized weight within half a step of the smoothed weight (P9 on W)
+    err = np.abs(ws - wq.astype(np.float64) * sc[:, None])
+    assert np.all(err <= sc[:, None] / 2 * (1 + 1e-6) + 1e-9)
+    # row sampling returns the same rows
+    wq2, sc2 = oracle.weight_quant(w, s, rows=[4, 2])
+    np.testing.assert_array_equal(wq2, wq[[4, 2]])
+    np.testing.assert_array_equal(sc2, sc[[4, 2]])
+
+
+def test_per_input_column_scale_is_rejected():
+    """The edge listing takes its weight maxima per input column but applies
+    the scale per output column in the GEMM; that cannot be factored out of
+    the contraction.  Our per-output-channel quantization reproduces Y, the
+    per-input reading applied per output does not (smoothed weights: the
+    outlier input channels carry much larger column peaks)."""
+    spec = datagen.workload(1).layers[0]
+    xc, x, w = datagen.calibration_x(spec), datagen.eval_x(spec), datagen.weights(spec)
+    s = oracle.calibrate(xc, w, spec.alpha)["s"]
+    y64 = oracle.ref_linear_f64(x, w)
+    xq, xs, _ = oracle.smooth_quantize_act(x, s=s)
+    wq, ws = oracle.weight_quant(w, s)
+    y_ok = oracle.gemm_w8a8(xq, xs, wq, ws)
+    wq_bad, cs = oracle.weight_quant_per_input(w, s)
+    y_bad = oracle.gemm_w8a8(xq, xs, wq_bad, cs[: spec.N])  # listing's indexing
+    rel = lambda y: np.linalg.norm(y - y64) / np.linalg.norm(y64)  # noqa: E731
+    assert rel(y_ok) < 0.05
+    assert rel(y_bad) > 5 * rel(y_ok)
+
+
+# ---- static scale -----------------------------------------------------------------
+
+@pytest.mark.parametrize("alpha", (0.0, 0.5, 0.85))
+def test_static_scale_equals_second_pass(alpha):
+    spec = datagen.workload(1).layers[0]
+    xc = datagen.calibration_x(spec)
+    a, wm = oracle.colmax(xc), oracle.colmax(datagen.weights(spec))
+    s = oracle.smooth_factor(a, wm, alpha)
+    second = np.abs(oracle.act_smooth(xc, s)).max()
+    assert oracle.static_scale(a, s) == np.float32(max(second, oracle.FLOOR)) / np.float32(127)
+
+
+# ---- integer GEMM (brute force) ---------------------------------------------------
+
+def test_all_int8_products():
+    v = np.arange(-128, 128, dtype=np.int8)
+    acc = oracle.gemm_i32(v[:, None], v[:, None])
+    np.testing.assert_array_equal(acc, np.outer(v.astype(np.int64), v.astype(np.int64)))
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (8, 8, 256), (7, 2, 64), (2, 7, 129)])
+def test_tiny_gemm_brute_force(shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    xq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    acc = oracle.gemm_i32(xq, wq)
+    for m in range(M):
+        for n in range(N):
+            t = 0
+            for k in range(K):
+                t += int(xq[m, k]) * int(wq[n, k])
+            assert acc[m, n] == t
+
+
+def test_gemm_int32_range_limit():
+    K = 133144  # 127^2 * K < 2^31
+    xq = np.full((1, K), 127, np.int8)
+    wq = np.full((2, K), -127, np.int8)
+    wq[1] = 127
+    acc = oracle.gemm_i32(xq, wq)
+    assert acc[0, 0] == -127 * 127 * K and acc[0, 1] == 127 * 127 * K
+    with pytest.raises(OverflowError):
+        oracle.gemm_i32(np.full((1, K + 1), 127, np.int8), np.full((1, K + 1), 127, np.int8))
+
+
+def test_dequant_within_two_ulps_of_exact_and_bf16_matches_torch():
+    rng = np.random.default_rng(4)
+    acc = rng.integers(-2**30, 2**30, size=(5, 9), dtype=np.int64).astype(np.int32)
+    xs = rng.uniform(1e-3, 1, 5).astype(np.float32)
+    ws = rng.uniform(1e-5, 1e-3, 9).astype(np.float32)
+    y = oracle.dequant(acc, xs, ws, per_token=True)
+    exact = acc.astype(np.float64) * xs[:, None].astype(np.float64) * ws[None, :].astype(np.float64)
+    assert np.all(np.abs(y - exact) <= 2.5 * np.spacing(np.abs(y)))
+    yt = oracle.dequant(acc, xs[:1], ws, per_token=False)
+    exact_t = acc.astype(np.float64) * float(xs[0]) * ws[None, :].astype(np.float64)
+    assert np.all(np.abs(yt - exact_t) <= 2.5 * np.spacing(np.abs(yt)))
+    # bf16 rounding vs torch's (nearest-even) conversion, incl. exact ties
+    vals = np.concatenate([y.ravel(), f32([1.0 + 2**-8, 1.0 + 3 * 2**-8, -1.0 - 2**-8, 0.0])])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_bf16(vals), ref)
+
+
+# ---- LayerNorm mode ---------------------------------------------------------------
+
+def test_canonical_sum_hand_cases():
+    _, cases = _golden("canonical_sum_cases.txt")
+    assert len(cases) == 5
+    for c in cases:
+        K, elems, expect = [t.strip() for t in c.split(";")]
+        v = np.zeros(int(K), np.float32)
+        for e in elems.split():
+            i, x = e.split(":")
+            v[int(i)] = float(x)
+        assert oracle.canonical_sum(v) == np.float32(float(expect)), c
+
+
+def test_canonical_sum_close_to_exact():
+    rng = np.random.default_rng(8)
+    for K in (64, 512, 4096, 8192, 12288):
+        v = rng.normal(0, 3, K).astype(np.float32)
+        exact = math.fsum(v.astype(np.float64))
+        bound = K * 2**-24 * np.abs(v.astype(np.float64)).sum()
+        assert abs(float(oracle.canonical_sum(v)) - exact) <= bound
+
+
+def test_layernorm_fold_against_fp64_layernorm():
+    """LN with (gamma/s, beta/s) equals LN(x; gamma, beta)/s ([Edge] §二) to
+    fp32 accuracy; the fp64 reference is numpy's mean/var, not the oracle."""
+    spec = datagen.workload(5).layers[0]
+    x = datagen.eval_x(spec, M=32)
+    gamma, beta = datagen.ln_params(spec)
+    rng = np.random.default_rng(12)
+    s = rng.uniform(0.05, 20.0, spec.K).astype(np.float32)
+    gs, bs = oracle.ln_fold(gamma, beta, s)
+    xh = oracle.act_ln(x, gs, bs, eps=1e-5)
+    xf = datagen.bf16_bits_to_f32(x).astype(np.float64)
+    mu = xf.mean(axis=1, keepdims=True)
+    var = xf.var(axis=1, keepdims=True)
+    ref = ((xf - mu) / np.sqrt(var + 1e-5) * gamma + beta) / s
+    scale = np.abs(ref).max(axis=1, keepdims=True)
+    assert np.all(np.abs(xh - ref) <= 4e-6 * scale)
+    # rows selection consistent
+    np.testing.assert_array_equal(oracle.act_ln(x, gs, bs, rows=[5, 1]), xh[[5, 1]])
+
+
+# ---- whole path: eq. (3) and error bounds -------------------------------------------
+
+def test_fp64_identity_config1():
+    spec = datagen.workload(1).layers[0]
+    xc, x, w = datagen.calibration_x(spec), datagen.eval_x(spec), datagen.weights(spec)
+    cal = oracle.calibrate(xc, w, spec.alpha)
+    y = oracle.ref_linear_f64(x, w)
+    yh = oracle.ref_smoothed_linear_f64(x, w, cal["s"])
+    assert np.linalg.norm(y - yh) / np.linalg.norm(y) <= 1e-12
+
+
+@pytest.mark.parametrize("s_one", [False, True])
+def test_output_error_bound_per_element(s_one):
+    """|y - Y64| <= sum_k(|xh_k| dw/2 + |wh_k| dx/2 + dx dw/4) + fp32 epilogue
+    rounding (quantizer bound of [Review] §2.2 on both operands)."""
+    spec = datagen.workload(1).layers[0]
+    xc, x, w = datagen.calibration_x(spec), datagen.eval_x(spec), datagen.weights(spec)
+    cal = oracle.calibrate(xc, w, spec.alpha)
+    s = np.ones(spec.K, np.float32) if s_one else cal["s"]
+    wq, ws = oracle.weight_quant(w, s)
+    xq, xs, _ = oracle.smooth_quantize_act(x, s=s)
+    y = oracle.gemm_w8a8(xq, xs, wq, ws)
+    xh = oracle.as_f64(x) / s.astype(np.float64)
+    wh = oracle.as_f64(w) * s.astype(np.float64)
+    y64 = xh @ wh.T
+    dx = xs.astype(np.float64)[:, None]
+    dw = ws.astype(np.float64)[None, :]
+    bound = (np.abs(xh).sum(1)[:, None] * dw / 2 + dx * np.abs(wh).sum(1)[None, :] / 2
+             + spec.K * dx * dw / 4)
+    bound = bound * (1 + 1e-5) + 4 * np.spacing(np.abs(y).astype(np.float32))
+    assert np.all(np.abs(y - y64) <= bound)
+    if s_one:  # no smoothing: the activation side is the identity
+        np.testing.assert_array_equal(oracle.act_smooth(x, s), x)
+
+
+def test_smoothing_reduces_error_on_outlier_layer():
+    """The point of the method: with outlier channels, alpha = 0.5 beats s = 1
+    (naive W8A8) on the static per-tensor setting of the single-linear case."""
+    spec = datagen.workload(1).layers[0]
+    xc, x, w = datagen.calibration_x(spec), datagen.eval_x(spec), datagen.weights(spec)
+    y64 = oracle.ref_linear_f64(x, w)
+
+    def run(s):
+        a = oracle.colmax(xc)
+        st = oracle.static_scale(a, s)
+        wq, ws = oracle.weight_quant(w, s)
+        xq, xs, _ = oracle.smooth_quantize_act(x, s=s, static=st)
+        y = oracle.gemm_w8a8(xq, xs, wq, ws, per_token=False)
+        return np.linalg.norm(y - y64) / np.linalg.norm(y64)
+
+    cal = oracle.calibrate(xc, w, 0.5)
+    e_sq = run(cal["s"])
+    e_naive = run(np.ones(spec.K, np.float32))
+    assert e_sq < 0.5 * e_naive
