@@ -1,0 +1,275 @@
+"""Benchmark of the SmoothQuant W8A8 linear-layer path on one MI355X.
+
+One step = one pass of the whole path over the OPT-6.7B-shaped prefill
+workload (M = 2048 tokens; linears qkv 4096->12288, out_proj 4096->4096,
+fc1 4096->16384, fc2 16384->4096; bf16 inputs, per-token activation scales,
+alpha = 0.5): for every linear, sq_calibrate (column absmax of the 512-token
+calibration set and of W, eq. (4), smoothed per-output-channel int8 weights),
+sq_smooth_quantize_act (X/s + per-token int8), sq_gemm_w8a8 (int8 GEMM with
+bf16 dequantized output).  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` = int8 TOPS of the whole step (2*M*N*K summed
+over the four linears / step time).  ``roofline`` describes the dominant
+kernel (the GEMM) measured with HIP events on the launch stream; the
+``cpu_baseline`` leg times the CPU oracle on a bounded sample of the same
+workload on this host.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload opt6.7b|...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SRC = os.path.join(ROOT, "w8a8_int8_gemm_colwise_amd", "csrc", "gemm.hip")
+
+WORKLOADS = {"opt6.7b": 2, "decode70b": 3, "opt175b": 4, "ln8192": 5, "single512": 1}
+
+
+def _bytes_of(dt: str) -> int:
+    return 2 if dt == "bf16" else 4
+
+
+def _alg(spec, M):
+    """Algorithmic bytes / ops per call for one linear."""
+    K, N, T = spec.K, spec.N, spec.T
+    bx, bw = _bytes_of(spec.x_dtype), _bytes_of(spec.w_dtype)
+    cal_bytes = (T * K * bx + 4 * K) + (N * K * bw + 4 * K) + (N * K * bw + N * K + 4 * N + 4 * K)
+    act_bytes = M * K * (bx + 1) + 4 * M + 4 * K
+    gemm_ops = 2.0 * M * N * K
+    gemm_bytes = M * K + N * K + 2 * M * N + 4 * M + 4 * N
+    return cal_bytes, act_bytes, gemm_ops, gemm_bytes
+
+
+def _traffic(gemm_launches: int):
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, valid
+    only while gemm.hip is the source the counters were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+        if t.get("gemm_source_sha256") != src:
+            return None
+        return t["gemm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(workload, max_tokens: int = 256):
+    """Time the CPU oracle on a bounded sample of the workload: every linear's
+    full calibration and weight quantization, then activation quantization,
+    int8 GEMM and dequant for the first ``max_tokens`` tokens."""
+    import datagen
+    import oracle
+
+    ops = 0.0
+    t_total = 0.0
+    for spec in workload.layers:
+        xc, w = datagen.calibration_x(spec), datagen.weights(spec)
+        x = datagen.eval_x(spec)[:max_tokens]
+        t0 = time.perf_counter()
+        cal = oracle.calibrate(xc, w, spec.alpha)
+        xq, xs, _ = oracle.smooth_quantize_act(x, s=cal["s"])
+        y = oracle.gemm_w8a8(xq, xs, cal["wq"], cal["w_scale"], out="bf16")
+        t_total += time.perf_counter() - t0
+        ops += 2.0 * x.shape[0] * spec.N * spec.K
+        del y
+    return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"every linear: full calibration + weight quantization, then activation "
+                       f"quantization + int8 GEMM + bf16 dequant of {max_tokens} of "
+                       f"{workload.layers[0].M} tokens; value = GEMM ops of the sample / "
+                       f"oracle wall time ({t_total:.1f} s)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="opt6.7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--decode-m", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU sharding).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import datagen
+    import w8a8_int8_gemm_colwise_amd as sq
+
+    cid = WORKLOADS[args.workload]
+    wl = datagen.workload(cid, M=args.decode_m) if cid == 3 else datagen.workload(cid)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    layers = []
+    for spec in wl.layers:
+        xc, w, x = datagen.calibration_x(spec), datagen.weights(spec), datagen.eval_x(spec)
+        L = dict(spec=spec, xc=to_dev(xc), w=to_dev(w), x=to_dev(x))
+        if spec.ln:
+            g, b = datagen.ln_params(spec)
+            L["g"], L["b"] = to_dev(g), to_dev(b)
+        K, N, M = spec.K, spec.N, x.shape[0]
+        f32 = dict(dtype=torch.float32, device=dev)
+        L["cal_out"] = dict(s=torch.empty(K, **f32), wq=torch.empty((N, K), dtype=torch.int8, device=dev),
+                            w_scale=torch.empty(N, **f32), static_scale=torch.empty(1, **f32),
+                            x_absmax=torch.empty(K, **f32), w_absmax=torch.empty(K, **f32))
+        if spec.ln:
+            L["cal_out"]["ln_gamma_s"] = torch.empty(K, **f32)
+            L["cal_out"]["ln_beta_s"] = torch.empty(K, **f32)
+        L["xq"] = torch.empty((M, K), dtype=torch.int8, device=dev)
+        L["xs"] = torch.empty(M, **f32)
+        L["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        L["M"] = M
+        layers.append(L)
+    del xc, w, x
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        for i, L in enumerate(layers):
+            spec = L["spec"]
+            if ev is not None:
+                ev[i][0].record(stream)
+            cal = sq.sq_calibrate(L["xc"], L["w"], spec.alpha, L.get("g"), L.get("b"),
+                                  out=L["cal_out"])
+            if ev is not None:
+                ev[i][1].record(stream)
+            if spec.ln:
+                sq.sq_smooth_quantize_act(L["x"], None, cal["ln_gamma_s"], cal["ln_beta_s"], 1e-5,
+                                          "per_token", xq=L["xq"], x_scale=L["xs"])
+            else:
+                sq.sq_smooth_quantize_act(L["x"], cal["s"], mode="per_token", xq=L["xq"],
+                                          x_scale=L["xs"])
+            if ev is not None:
+                ev[i][2].record(stream)
+            sq.sq_gemm_w8a8(L["xq"], L["xs"], cal["wq"], cal["w_scale"], "per_token", "bf16",
+                            y=L["y"])
+            if ev is not None:
+                ev[i][3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events around every call on the launch stream
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    n = len(layers)
+    t_cal = np.zeros(n)
+    t_act = np.zeros(n)
+    t_gemm = np.zeros(n)
+    for k in range(args.steps):
+        for i in range(n):
+            e = evs[k][i]
+            t_cal[i] += e[0].elapsed_time(e[1]) * 1e-3
+            t_act[i] += e[1].elapsed_time(e[2]) * 1e-3
+            t_gemm[i] += e[2].elapsed_time(e[3]) * 1e-3
+    t_cal /= args.steps
+    t_act /= args.steps
+    t_gemm /= args.steps
+
+    ms_per_step = elapsed / args.steps * 1e3
+    tot_ops = 0.0
+    per = {}
+    cal_b = act_b = gemm_ops = 0.0
+    for i, L in enumerate(layers):
+        spec = L["spec"]
+        cb, ab, go, gb = _alg(spec, L["M"])
+        tot_ops += go
+        cal_b += cb
+        act_b += ab
+        gemm_ops += go
+        per[spec.name] = {
+            "shape_MNK": [L["M"], spec.N, spec.K],
+            "calibrate_us": round(t_cal[i] * 1e6, 2),
+            "calibrate_GBs": round(cb / t_cal[i] / 1e9, 1),
+            "act_quant_us": round(t_act[i] * 1e6, 2),
+            "act_quant_GBs": round(ab / t_act[i] / 1e9, 1),
+            "gemm_us": round(t_gemm[i] * 1e6, 2),
+            "gemm_TOPS": round(go / t_gemm[i] / 1e12, 1),
+            "gemm_GBs_alg": round(gb / t_gemm[i] / 1e9, 1),
+        }
+    value = tot_ops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel by time: the GEMM (MFMA-bound) unless the HBM-bound
+    # calls take longer
+    tg, tc, ta = t_gemm.sum(), t_cal.sum(), t_act.sum()
+    launches = n
+    if tg >= max(tc, ta):
+        ach = gemm_ops / tg / 1e12
+        traffic = _traffic(launches)
+        roof = {"kernel": "sq_gemm_w8a8 (gemm_kernel)", "bound": "mfma", "achieved": round(ach, 1),
+                "peak": PEAK_INT8_TOPS, "unit": "TOPS", "frac": round(ach / PEAK_INT8_TOPS, 4),
+                "traffic": traffic, "launches_per_step": launches,
+                "avg_launch_us": round(tg / launches * 1e6, 2),
+                "alg_ops_per_launch": gemm_ops / launches}
+    else:
+        name, t, b = ("sq_calibrate", tc, cal_b) if tc >= ta else ("sq_smooth_quantize_act", ta, act_b)
+        ach = b / t / 1e9
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "launches_per_step": launches, "avg_launch_us": round(t / launches * 1e6, 2),
+                "alg_bytes_per_launch": b / launches}
+
+    out = {
+        "metric": "W8A8 GEMM INT8 TOPS (% MFMA peak) + fused quantize GB/s (% HBM peak)",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded; outlier channels at +-U(50,120); bf16 inputs)",
+        "config": {"workload": wl.name, "M": layers[0]["M"],
+                   "linears_KN": [[L["spec"].K, L["spec"].N] for L in layers],
+                   "alpha": wl.layers[0].alpha, "act_scale": "per_token", "y_dtype": "bf16",
+                   "step": "sq_calibrate + sq_smooth_quantize_act + sq_gemm_w8a8 per linear"},
+        "roofline": roof,
+        "gemm": {"TOPS": round(gemm_ops / tg / 1e12, 1),
+                 "frac": round(gemm_ops / tg / 1e12 / PEAK_INT8_TOPS, 4)},
+        "act_quant": {"GBs": round(act_b / ta / 1e9, 1),
+                      "frac": round(act_b / ta / 1e9 / PEAK_HBM_GBS, 4)},
+        "calibrate": {"GBs": round(cal_b / tc / 1e9, 1),
+                      "frac": round(cal_b / tc / 1e9 / PEAK_HBM_GBS, 4)},
+        "per_linear": per,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * sq.h -- C ABI of the SmoothQuant W8A8 linear-layer library for MI355X
+ * (gfx950).  libsq.so implements every call with hand-written HIP kernels.
+ *
+ * The calls follow the smoothing rewrite of a linear layer,
+ *     Y = X W = (X diag(s)^-1) (diag(s) W)
+ * ([Review] "SmoothQuant：大型语言模型的精准高效训练后量化 — 深度技术评审",
+ * §5.1 eq. (3)), split into the offline half (calibrate, smooth and quantize
+ * the weights; [Teach] "SmoothQuant 如何解决激活量化难题？为什么适合 W8A8？",
+ * §四) and the runtime half (smooth + quantize the activation, then the int8
+ * GEMM with a dequantizing epilogue; [Edge] "嵌入式 SLM 动态权重量化：
+ * SmoothQuant 激活异常值迁移与 INT8 部署实战", §二 runtime graph).
+ *
+ * Conventions shared by every call
+ *   - Layouts are row-major.  X is [tokens, K]; W is stored [N, K] (output
+ *     channel x input channel, as in the edge article's GEMM listing), so the
+ *     layer computes Y[m, n] = sum_k X[m, k] W[n, k].
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates nothing and keeps no state between calls; calls are
+ *     re-entrant.  Inputs are never written.
+ *   - Every call validates its arguments on the host first and returns a
+ *     status without touching the device when they are invalid.  Otherwise it
+ *     enqueues its kernels on `stream` (0 = the null stream) and returns
+ *     without waiting; a fault inside a kernel surfaces at the caller's next
+ *     synchronisation.  SQ_ERR_HIP means a launch was rejected.
+ *   - Pointers must be 16-byte aligned; K must be a multiple of 64 and at most
+ *     SQ_MAX_K (so that 127*127*K fits in int32); other sizes may be 0 (the
+ *     call then does nothing or writes only the size-K outputs).
+ *   - Inputs are assumed finite; results for NaN/Inf inputs, or for inputs
+ *     whose smoothed values overflow fp32, are unspecified.
+ *
+ * Numerical contract (RN = one IEEE binary32 operation, round to nearest
+ * even; rne = round to nearest integer, ties to even; clamp = to [-127, 127];
+ * FLOOR = SQ_ABSMAX_FLOOR).  Every listed value is produced bit for bit:
+ *   a_j  = max(FLOOR, max_t |x_cal[t, j]|)          w_j = max(FLOOR, max_n |W[n, j]|)
+ *   s_j  = RN32( pow64(a_j, alpha) / pow64(w_j, 1 - alpha) )   (fp64, one rounding)
+ *   What = RN(W[n,k] * s_k);  dw_n = RN(max(FLOOR, max_k |What|) / 127)
+ *   wq   = clamp(rne(RN(What / dw_n)))
+ *   g'_k = RN(gamma_k / s_k), b'_k = RN(beta_k / s_k)
+ *   dx_static = RN(max(FLOOR, max_k RN(a_k / s_k)) / 127)
+ *   plain mode:  xh_k = RN(x_k / s_k)
+ *   LN mode:     mu = RN(S(x)/K); d_k = RN(x_k - mu); var = RN(S(RN(d*d))/K);
+ *                rho = RN(1 / RN(sqrt(RN(var + eps))));
+ *                xh_k = RN(RN(RN(d_k * rho) * g'_k) + b'_k)
+ *                where S(v) is the canonical sum: 256 fp32 partials, element k
+ *                added to partial floor(k/8) mod 256 in increasing k from +0,
+ *                then p[i] = RN(p[i] + p[i+d]) for d = 128, 64, ..., 1.
+ *   per-token:   dx_t = RN(max(FLOOR, max_k |xh_k|) / 127);  static: dx_t = dx_static
+ *   xq   = clamp(rne(RN(xh_k / dx_t)))
+ *   acc  = sum_k xq[t,k] * wq[n,k]   (exact int32)
+ *   y    = RN(RN_f32(acc) * RN(dx_t * dw_n));  bf16 output = y rounded to
+ *          bf16 (nearest even).
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* sq_stream_t; /* a hipStream_t */
+
+#define SQ_ABI_VERSION 1
+#define SQ_MAX_K 133120          /* largest multiple of 64 with 127*127*K < 2^31 */
+#define SQ_ABSMAX_FLOOR 1e-7f    /* floor of every absolute maximum */
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_ERR_NULL_ARG = 1,  /* a required pointer is NULL */
+    SQ_ERR_BAD_SHAPE = 2, /* negative size, K % 64 != 0, K > SQ_MAX_K, ... */
+    SQ_ERR_BAD_DTYPE = 3, /* dtype not allowed for that operand */
+    SQ_ERR_BAD_ALPHA = 4, /* alpha outside [0, 1] or not finite */
+    SQ_ERR_ALIGNMENT = 5, /* pointer not 16-byte aligned */
+    SQ_ERR_HIP = 6,       /* the HIP runtime rejected a launch */
+    SQ_ERR_BAD_MODE = 7   /* unknown mode, or a mode/argument combination */
+} sq_status;
+
+typedef enum { SQ_F32 = 0, SQ_BF16 = 1, SQ_I8 = 2, SQ_I32 = 3 } sq_dtype;
+
+typedef enum { SQ_PER_TOKEN = 0, SQ_STATIC_PER_TENSOR = 1 } sq_act_mode;
+
+/*
+ * sq_calibrate -- the offline half.
+ *   [Teach] §四 (collect calibration peaks, compute the smoothing scale,
+ *   adjust the weights offline); [Review] §5.3 eq. (4) (s_j); [Edge] §二-§三
+ *   (fold 1/s into the LayerNorm's gamma/beta, fold s into W, quantize W to
+ *   int8 offline with one scale per channel -- here per OUTPUT channel).
+ *
+ *   x_cal [T, K]  calibration activations (dtype x_dt: F32 or BF16), T >= 0
+ *   w     [N, K]  weight, output channel x input channel (F32 or BF16), N >= 0
+ *   alpha         migration strength in [0, 1]
+ *   ln_gamma, ln_beta [K] fp32: the LayerNorm in front of the layer, or both
+ *                 NULL when there is none
+ * Outputs (device, caller-owned):
+ *   s [K] fp32            smoothing factor
+ *   wq [N, K] int8        smoothed, quantized weight
+ *   w_scale [N] fp32      dw_n per output channel
+ *   act_scale_static [1]  dx_static (may be NULL)
+ *   ln_gamma_s, ln_beta_s [K] fp32: folded LayerNorm (required iff ln_gamma)
+ *   x_absmax, w_absmax [K] fp32: a_j and w_j (required; they also serve as the
+ *                 library's working memory for the two column maxima)
+ * Kernels: a fill of the maxima, two column-absmax passes, the factor pass,
+ * one weight smooth+quantize pass.  Reads X_cal and W once each from HBM.
+ */
+sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T,
+                       const void* w, sq_dtype w_dt, int64_t N, int64_t K, float alpha,
+                       const float* ln_gamma, const float* ln_beta,
+                       float* s, int8_t* wq, float* w_scale, float* act_scale_static,
+                       float* ln_gamma_s, float* ln_beta_s,
+                       float* x_absmax, float* w_absmax, sq_stream_t stream);
+
+/*
+ * sq_smooth_quantize_act -- runtime activation side.
+ *   [Review] §5.1 eq. (3) (X diag(s)^-1); [Edge] §二 (LayerNorm with gamma/s,
+ *   beta/s emits the smoothed activation, then int8 quantization); [Review]
+ *   §2.5-§2.6 (dynamic per-token or static per-tensor scale).
+ *
+ *   x [M, K]  activation (F32 or BF16).  Plain mode: the input of the linear.
+ *             LayerNorm mode: the input of the LayerNorm.
+ *   s [K]     plain mode (then ln_gamma_s and ln_beta_s are NULL), or NULL
+ *   ln_gamma_s, ln_beta_s [K]  LayerNorm mode (then s is NULL); ln_eps > 0
+ *   mode      SQ_PER_TOKEN: x_scale [M] receives dx_t.
+ *             SQ_STATIC_PER_TENSOR: static_scale [1] (device) holds dx_static;
+ *             x_scale may be NULL and is not written.
+ *   xq [M, K] int8 output codes.
+ * One kernel; reads X once and writes xq (and x_scale) once.
+ */
+sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                                 const float* s, const float* ln_gamma_s,
+                                 const float* ln_beta_s, float ln_eps,
+                                 sq_act_mode mode, const float* static_scale,
+                                 int8_t* xq, float* x_scale, sq_stream_t stream);
+
+/*
+ * sq_gemm_w8a8 -- int8 x int8 GEMM with int32 accumulation and the
+ * dequantizing epilogue.  [Edge] §三 (GEMM listing: int32 accumulator of
+ * activation code times weight code with W stored [out][in]; output =
+ * (float)acc * (act_scale * weight_scale[n])); [Review] §2.6 / Fig. 3 (scales
+ * only on the outer dimensions: token and output channel).
+ *
+ *   xq [M, K] int8, x_scale: [M] when x_mode = SQ_PER_TOKEN, [1] when static
+ *   wq [N, K] int8, w_scale [N]
+ *   y  [M, N] of y_dt: SQ_F32, SQ_BF16, or SQ_I32 (the raw accumulators,
+ *      x_scale and w_scale then unused and may be NULL)
+ * Runs on the gfx950 int8 matrix cores (MFMA), LDS-staged K tiles.
+ */
+sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_mode x_mode,
+                       const int8_t* wq, const float* w_scale,
+                       int64_t M, int64_t N, int64_t K,
+                       void* y, sq_dtype y_dt, sq_stream_t stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* sq_status_string(sq_status status);
+
+/* SQ_ABI_VERSION of the loaded library. */
+int sq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SQ_H */

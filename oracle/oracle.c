@@ -61,14 +61,19 @@ int orc_num_threads(void) { return omp_get_max_threads(); }
  * Column k of a row-major [rows, K] tensor is input channel k (for W stored
  * [out][in] as in the edge listing, column k is input channel k too). */
 void orc_colmax(const void* x, int dt, int64_t rows, int64_t K, float* out) {
+    /* columns are split into blocks across threads; each block is swept row
+     * by row so the reads follow the row-major layout */
+    const int64_t BLK = 256;
 #pragma omp parallel for schedule(static)
-    for (int64_t k = 0; k < K; ++k) {
-        float m = ORC_FLOOR;
+    for (int64_t k0 = 0; k0 < K; k0 += BLK) {
+        int64_t k1 = (k0 + BLK < K) ? k0 + BLK : K;
+        for (int64_t k = k0; k < k1; ++k) out[k] = ORC_FLOOR;
         for (int64_t r = 0; r < rows; ++r) {
-            float v = fabsf(load_elem(x, dt, r * K + k));
-            if (v > m) m = v;
+            for (int64_t k = k0; k < k1; ++k) {
+                float v = fabsf(load_elem(x, dt, r * K + k));
+                if (v > out[k]) out[k] = v;
+            }
         }
-        out[k] = m;
     }
 }
 

@@ -1,0 +1,137 @@
+"""Host-side checks of libsq.so that need no GPU: the library loads, exports
+every entry point include/sq.h declares, and rejects invalid arguments with the
+documented status before touching the device (so only fake, never-dereferenced
+pointers are passed here, and only to calls that must fail validation)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import w8a8_int8_gemm_colwise_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sq.h")
+
+P = 0x1000      # aligned fake device pointer (never dereferenced: validation fails first)
+MIS = 0x1008    # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sq_status|const char\s*\*|int)\s+(sq_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_loads_and_version():
+    L = sq.lib()
+    assert L.sq_abi_version() == sq.SQ_ABI_VERSION
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"sq_calibrate", "sq_smooth_quantize_act", "sq_gemm_w8a8",
+                          "sq_status_string", "sq_abi_version"}
+    L = sq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", sq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (sq_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    assert set(sq.EXPORTED) <= exported
+
+
+def test_status_strings():
+    L = sq.lib()
+    for code in range(8):
+        s = L.sq_status_string(code).decode()
+        assert s.startswith("SQ_")
+    assert L.sq_status_string(99).decode() == "SQ_ERR_UNKNOWN"
+
+
+def _gemm(M=4, N=4, K=64, xq=P, xs=P, mode=0, wq=P, ws=P, y=P, ydt=0):
+    return sq.lib().sq_gemm_w8a8(xq, xs, mode, wq, ws, M, N, K, y, ydt, None)
+
+
+def _act(M=4, K=64, x=P, dt=1, s=P, g=None, b=None, eps=1e-5, mode=0, st=None, xq=P, xs=P):
+    return sq.lib().sq_smooth_quantize_act(x, dt, M, K, s, g, b, eps, mode, st, xq, xs, None)
+
+
+def _cal(T=8, N=8, K=64, alpha=0.5, xdt=1, wdt=1, g=None, b=None, gs=None, bs=None, x=P, w=P,
+         s=P, wq=P, wsc=P, st=P, xa=P, wa=P):
+    return sq.lib().sq_calibrate(x, xdt, T, w, wdt, N, K, alpha, g, b, s, wq, wsc, st, gs, bs,
+                                 xa, wa, None)
+
+
+@pytest.mark.parametrize("K", [0, -64, 63, 65, 100, sq.SQ_MAX_K + 64])
+def test_gemm_rejects_bad_k(K):
+    assert _gemm(K=K) == 2
+
+
+def test_gemm_validation():
+    assert _gemm(M=-1) == 2
+    assert _gemm(N=-1) == 2
+    assert _gemm(ydt=7) == 3
+    assert _gemm(ydt=2) == 3          # int8 output is not an output type
+    assert _gemm(mode=5) == 7
+    assert _gemm(xq=None) == 1
+    assert _gemm(wq=None) == 1
+    assert _gemm(y=None) == 1
+    assert _gemm(xs=None) == 1        # dequant needs scales
+    assert _gemm(ws=None) == 1
+    assert _gemm(xq=MIS) == 5
+    assert _gemm(y=MIS) == 5
+    # M = 0 or N = 0: nothing to do, succeeds without touching the device
+    assert _gemm(M=0, xq=None, y=None) == 0
+    assert _gemm(N=0, wq=None, y=None) == 0
+
+
+def test_act_validation():
+    assert _act(K=96) == 2
+    assert _act(M=-3) == 2
+    assert _act(dt=2) == 3
+    assert _act(mode=2) == 7
+    assert _act(s=None) == 1                           # neither plain nor LN
+    assert _act(g=P, b=P) == 7                         # both plain and LN
+    assert _act(s=None, g=P, b=None) == 1              # half of LN
+    assert _act(s=None, g=P, b=P, eps=0.0) == 7
+    assert _act(s=None, g=P, b=P, eps=float("nan")) == 7
+    assert _act(mode=1, st=None) == 1                  # static mode needs the scale
+    assert _act(xs=None) == 1                          # per-token mode writes scales
+    assert _act(x=MIS) == 5
+    assert _act(xq=MIS) == 5
+    assert _act(M=0, x=None, xq=None, xs=None) == 0
+
+
+def test_calibrate_validation():
+    assert _cal(K=32) == 2
+    assert _cal(T=-1) == 2
+    assert _cal(N=-1) == 2
+    assert _cal(xdt=3) == 3
+    assert _cal(wdt=2) == 3
+    for a in (-0.01, 1.01, float("nan"), float("inf")):
+        assert _cal(alpha=a) == 4
+    assert _cal(s=None) == 1
+    assert _cal(xa=None) == 1
+    assert _cal(wa=None) == 1
+    assert _cal(x=None) == 1
+    assert _cal(wq=None) == 1
+    assert _cal(g=P, b=None) == 7                      # gamma without beta
+    assert _cal(g=P, b=P, gs=None, bs=P) == 1          # fold outputs required
+    assert _cal(wsc=MIS) == 5
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sq.sq_smooth_quantize_act(x, s=torch.ones(64))
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(sq, "_lib", None)
+    monkeypatch.setattr(sq, "LIB_PATH", str(tmp_path / "libsq.so"))
+    with pytest.raises(RuntimeError):
+        sq.lib()

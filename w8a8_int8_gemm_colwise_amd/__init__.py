@@ -1,0 +1,177 @@
+"""Python binding of libsq.so, the MI355X (gfx950) SmoothQuant W8A8 library.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory (output tensors are allocated with
+``torch.empty`` on the input's device) and the current HIP stream.  The
+functions carry the C ABI's names (include/sq.h):
+
+  sq_calibrate            offline: column absmax of X_cal and W, eq. (4)
+                          smoothing factor, LayerNorm fold, static scale,
+                          smoothed per-output-channel int8 weights
+  sq_smooth_quantize_act  runtime: X/s (or the folded LayerNorm), then
+                          per-token or static per-tensor int8
+  sq_gemm_w8a8            runtime: int8 GEMM, int32 accumulation, dequant
+
+There is no fallback: if libsq.so is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsq.so")
+
+SQ_F32, SQ_BF16, SQ_I8, SQ_I32 = 0, 1, 2, 3
+SQ_PER_TOKEN, SQ_STATIC_PER_TENSOR = 0, 1
+SQ_MAX_K = 133120
+SQ_ABI_VERSION = 1
+EXPORTED = ("sq_calibrate", "sq_smooth_quantize_act", "sq_gemm_w8a8", "sq_status_string",
+            "sq_abi_version")
+
+_lib = None
+
+
+class SQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsq.so (built by ``python -m w8a8_int8_gemm_colwise_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run python -m w8a8_int8_gemm_colwise_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci, cf = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.sq_calibrate.restype = ci
+    L.sq_calibrate.argtypes = [vp, ci, i64, vp, ci, i64, i64, cf, vp, vp, vp, vp, vp, vp, vp, vp,
+                               vp, vp, vp]
+    L.sq_smooth_quantize_act.restype = ci
+    L.sq_smooth_quantize_act.argtypes = [vp, ci, i64, i64, vp, vp, vp, cf, ci, vp, vp, vp, vp]
+    L.sq_gemm_w8a8.restype = ci
+    L.sq_gemm_w8a8.argtypes = [vp, vp, ci, vp, vp, i64, i64, i64, vp, ci, vp]
+    L.sq_status_string.restype = ctypes.c_char_p
+    L.sq_status_string.argtypes = [ci]
+    L.sq_abi_version.restype = ci
+    L.sq_abi_version.argtypes = []
+    if L.sq_abi_version() != SQ_ABI_VERSION:
+        raise RuntimeError("libsq.so ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise SQError(rc, lib().sq_status_string(rc).decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SQ_F32
+    if t.dtype == torch.bfloat16:
+        return SQ_BF16
+    raise TypeError(f"activation/weight dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev2d(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D tensor")
+
+
+def _mode(mode) -> int:
+    if mode in ("per_token", SQ_PER_TOKEN):
+        return SQ_PER_TOKEN
+    if mode in ("static", SQ_STATIC_PER_TENSOR):
+        return SQ_STATIC_PER_TENSOR
+    raise ValueError(f"unknown activation mode {mode!r}")
+
+
+def sq_calibrate(x_cal: torch.Tensor, w: torch.Tensor, alpha: float,
+                 ln_gamma: torch.Tensor | None = None, ln_beta: torch.Tensor | None = None,
+                 out: dict | None = None) -> dict:
+    """Offline half: returns dict(s, wq, w_scale, static_scale, x_absmax, w_absmax
+    [, ln_gamma_s, ln_beta_s]).  ``out`` may supply preallocated tensors."""
+    _dev2d(x_cal, "x_cal")
+    _dev2d(w, "w")
+    T, K = x_cal.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError("x_cal and w disagree on K")
+    dev = w.device
+    o = dict(out or {})
+    f32 = dict(dtype=torch.float32, device=dev)
+    o.setdefault("s", torch.empty(K, **f32))
+    o.setdefault("wq", torch.empty((N, K), dtype=torch.int8, device=dev))
+    o.setdefault("w_scale", torch.empty(N, **f32))
+    o.setdefault("static_scale", torch.empty(1, **f32))
+    o.setdefault("x_absmax", torch.empty(K, **f32))
+    o.setdefault("w_absmax", torch.empty(K, **f32))
+    if ln_gamma is not None:
+        o.setdefault("ln_gamma_s", torch.empty(K, **f32))
+        o.setdefault("ln_beta_s", torch.empty(K, **f32))
+    _check(lib().sq_calibrate(
+        _ptr(x_cal), _dt(x_cal), T, _ptr(w), _dt(w), N, K, float(alpha),
+        _ptr(ln_gamma), _ptr(ln_beta), _ptr(o["s"]), _ptr(o["wq"]), _ptr(o["w_scale"]),
+        _ptr(o["static_scale"]), _ptr(o.get("ln_gamma_s")), _ptr(o.get("ln_beta_s")),
+        _ptr(o["x_absmax"]), _ptr(o["w_absmax"]), _stream(dev)))
+    return o
+
+
+def sq_smooth_quantize_act(x: torch.Tensor, s: torch.Tensor | None = None,
+                           ln_gamma_s: torch.Tensor | None = None,
+                           ln_beta_s: torch.Tensor | None = None, ln_eps: float = 1e-5,
+                           mode="per_token", static_scale: torch.Tensor | None = None,
+                           xq: torch.Tensor | None = None, x_scale: torch.Tensor | None = None):
+    """Runtime activation side: returns (xq int8 [M,K], x_scale fp32 [M] or the
+    static scale [1])."""
+    _dev2d(x, "x")
+    M, K = x.shape
+    md = _mode(mode)
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if md == SQ_PER_TOKEN and x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib().sq_smooth_quantize_act(
+        _ptr(x), _dt(x), M, K, _ptr(s), _ptr(ln_gamma_s), _ptr(ln_beta_s), float(ln_eps), md,
+        _ptr(static_scale), _ptr(xq), _ptr(x_scale) if md == SQ_PER_TOKEN else None,
+        _stream(x.device)))
+    return xq, (x_scale if md == SQ_PER_TOKEN else static_scale)
+
+
+_OUT = {"f32": (SQ_F32, torch.float32), "bf16": (SQ_BF16, torch.bfloat16),
+        "i32": (SQ_I32, torch.int32)}
+
+
+def sq_gemm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor,
+                 w_scale: torch.Tensor | None, mode="per_token", out_dtype: str = "bf16",
+                 y: torch.Tensor | None = None) -> torch.Tensor:
+    """Int8 GEMM + dequant: y[M,N] = RN(float(acc) * RN(dx_t * dw_n))."""
+    _dev2d(xq, "xq")
+    _dev2d(wq, "wq")
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K != K2:
+        raise ValueError("xq and wq disagree on K")
+    code, tdt = _OUT[out_dtype]
+    if y is None:
+        y = torch.empty((M, N), dtype=tdt, device=xq.device)
+    _check(lib().sq_gemm_w8a8(_ptr(xq), _ptr(x_scale), _mode(mode), _ptr(wq), _ptr(w_scale),
+                              M, N, K, _ptr(y), code, _stream(xq.device)))
+    return y

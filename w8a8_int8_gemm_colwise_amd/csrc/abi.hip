@@ -1,0 +1,113 @@
+// abi.hip -- the C ABI of libsq.so: host-side validation, then the launchers.
+// See include/sq.h for the contract of every entry point.
+#include "../../include/sq.h"
+
+#include <cmath>
+
+#include "sq_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_k(int64_t K) { return K > 0 && K % 64 == 0 && K <= SQ_MAX_K; }
+
+bool valid_rows(int64_t r) { return r >= 0 && r <= 0x7fffffffLL; }
+
+bool float_dtype(sq_dtype d) { return d == SQ_F32 || d == SQ_BF16; }
+
+sq::Dt to_dt(sq_dtype d) { return d == SQ_BF16 ? sq::Dt::BF16 : sq::Dt::F32; }
+
+sq_status from_hip(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T, const void* w, sq_dtype w_dt,
+                       int64_t N, int64_t K, float alpha, const float* ln_gamma,
+                       const float* ln_beta, float* s, int8_t* wq, float* w_scale,
+                       float* act_scale_static, float* ln_gamma_s, float* ln_beta_s,
+                       float* x_absmax, float* w_absmax, sq_stream_t stream) {
+    if (!valid_k(K) || !valid_rows(T) || !valid_rows(N)) return SQ_ERR_BAD_SHAPE;
+    if (!float_dtype(x_dt) || !float_dtype(w_dt)) return SQ_ERR_BAD_DTYPE;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_BAD_ALPHA;
+    if (!s || !x_absmax || !w_absmax) return SQ_ERR_NULL_ARG;
+    if (T > 0 && !x_cal) return SQ_ERR_NULL_ARG;
+    if (N > 0 && (!w || !wq || !w_scale)) return SQ_ERR_NULL_ARG;
+    if ((ln_gamma == nullptr) != (ln_beta == nullptr)) return SQ_ERR_BAD_MODE;
+    if (ln_gamma && (!ln_gamma_s || !ln_beta_s)) return SQ_ERR_NULL_ARG;
+    const void* ptrs[] = {x_cal, w, ln_gamma, ln_beta, s, wq, w_scale, act_scale_static,
+                          ln_gamma_s, ln_beta_s, x_absmax, w_absmax};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
+    return from_hip(sq::launch_calibrate(
+        x_cal, to_dt(x_dt), T, w, to_dt(w_dt), N, K, alpha, ln_gamma, ln_beta, s, wq, w_scale,
+        act_scale_static, ln_gamma ? ln_gamma_s : nullptr, ln_gamma ? ln_beta_s : nullptr,
+        x_absmax, w_absmax, reinterpret_cast<hipStream_t>(stream)));
+}
+
+sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                                 const float* s, const float* ln_gamma_s,
+                                 const float* ln_beta_s, float ln_eps, sq_act_mode mode,
+                                 const float* static_scale, int8_t* xq, float* x_scale,
+                                 sq_stream_t stream) {
+    if (!valid_k(K) || !valid_rows(M)) return SQ_ERR_BAD_SHAPE;
+    if (!float_dtype(x_dt)) return SQ_ERR_BAD_DTYPE;
+    if (mode != SQ_PER_TOKEN && mode != SQ_STATIC_PER_TENSOR) return SQ_ERR_BAD_MODE;
+    const bool ln = (ln_gamma_s != nullptr) || (ln_beta_s != nullptr);
+    if (ln) {
+        if (s) return SQ_ERR_BAD_MODE;
+        if (!ln_gamma_s || !ln_beta_s) return SQ_ERR_NULL_ARG;
+        if (!(ln_eps > 0.0f) || !std::isfinite(ln_eps)) return SQ_ERR_BAD_MODE;
+    } else if (!s) {
+        return SQ_ERR_NULL_ARG;
+    }
+    if (mode == SQ_STATIC_PER_TENSOR && !static_scale) return SQ_ERR_NULL_ARG;
+    if (M > 0 && (!x || !xq)) return SQ_ERR_NULL_ARG;
+    if (M > 0 && mode == SQ_PER_TOKEN && !x_scale) return SQ_ERR_NULL_ARG;
+    const void* ptrs[] = {x, s, ln_gamma_s, ln_beta_s, static_scale, xq, x_scale};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
+    return from_hip(sq::launch_act_quant(x, to_dt(x_dt), M, K, ln ? nullptr : s, ln_gamma_s,
+                                         ln_beta_s, ln_eps, mode == SQ_STATIC_PER_TENSOR,
+                                         static_scale, xq, x_scale,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_mode x_mode,
+                       const int8_t* wq, const float* w_scale, int64_t M, int64_t N, int64_t K,
+                       void* y, sq_dtype y_dt, sq_stream_t stream) {
+    if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return SQ_ERR_BAD_SHAPE;
+    if (M * N > (int64_t(1) << 40)) return SQ_ERR_BAD_SHAPE;
+    if (y_dt != SQ_F32 && y_dt != SQ_BF16 && y_dt != SQ_I32) return SQ_ERR_BAD_DTYPE;
+    if (x_mode != SQ_PER_TOKEN && x_mode != SQ_STATIC_PER_TENSOR) return SQ_ERR_BAD_MODE;
+    if (M > 0 && N > 0) {
+        if (!xq || !wq || !y) return SQ_ERR_NULL_ARG;
+        if (y_dt != SQ_I32 && (!x_scale || !w_scale)) return SQ_ERR_NULL_ARG;
+    }
+    const void* ptrs[] = {xq, x_scale, wq, w_scale, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
+    const int out = (y_dt == SQ_F32) ? 0 : (y_dt == SQ_BF16) ? 1 : 2;
+    return from_hip(sq::launch_gemm(xq, x_scale, x_mode == SQ_PER_TOKEN, wq, w_scale, M, N, K,
+                                    y, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* sq_status_string(sq_status status) {
+    switch (status) {
+        case SQ_OK: return "SQ_OK";
+        case SQ_ERR_NULL_ARG: return "SQ_ERR_NULL_ARG: a required pointer is NULL";
+        case SQ_ERR_BAD_SHAPE: return "SQ_ERR_BAD_SHAPE: invalid size (K must be a positive multiple of 64 up to SQ_MAX_K; sizes non-negative)";
+        case SQ_ERR_BAD_DTYPE: return "SQ_ERR_BAD_DTYPE: dtype not allowed for this operand";
+        case SQ_ERR_BAD_ALPHA: return "SQ_ERR_BAD_ALPHA: alpha must lie in [0, 1]";
+        case SQ_ERR_ALIGNMENT: return "SQ_ERR_ALIGNMENT: pointers must be 16-byte aligned";
+        case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime rejected a kernel launch";
+        case SQ_ERR_BAD_MODE: return "SQ_ERR_BAD_MODE: invalid mode or mode/argument combination";
+    }
+    return "SQ_ERR_UNKNOWN";
+}
+
+int sq_abi_version(void) { return SQ_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,381 @@
+// act_quant.hip -- runtime activation side: smooth, then int8-quantize, in one
+// HBM pass.
+//
+//   [Review] "SmoothQuant：大型语言模型的精准高效训练后量化 — 深度技术评审"
+//   §5.1 eq. (3): the activation is divided per input channel by s
+//   (X diag(s)^-1); §2.2 the symmetric quantizer (step = max|X|/127, round to
+//   nearest); §2.5 dynamic vs static scales; §2.6 / Fig. 3 per-token scales.
+//   [Edge] "嵌入式 SLM 动态权重量化：SmoothQuant 激活异常值迁移与 INT8 部署实战"
+//   §二: the LayerNorm with gamma/s and beta/s folded in emits the smoothed
+//   activation directly, followed by int8 quantization.
+//
+// One token row per block.  The block's lanes own fixed chunks of 8 elements
+// (chunk c = tid + i*blockDim), so per-column data (1/s_k) is computed once
+// per block and reused across the rows the block walks.  The row stays in
+// registers between the absmax reduction and the quantize pass.  Divisions
+// by s_k and by the step use div_rn() (correctly rounded, five VALU ops).
+// LayerNorm mode uses exactly 256 lanes so that lane t owns partial t of the
+// canonical fp32 reduction (chunk c -> partial c mod 256, increasing k within
+// a partial, then the fixed halving tree).
+#include <algorithm>
+
+#include "sq_device.hpp"
+#include "sq_internal.hpp"
+
+namespace sq {
+namespace {
+
+constexpr int kLnThreads = 256;
+
+// Block-wide max of non-negative values; every lane receives the result.
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int nw = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float m = red[0];
+    for (int i = 1; i < nw; ++i) m = fmaxf(m, red[i]);
+    __syncthreads();
+    return m;
+}
+
+// Canonical halving tree over the 256 lane partials:
+// p[i] = p[i] + p[i+d] for d = 128, 64, ..., 1.  Every lane gets p[0].
+__device__ __forceinline__ float canonical_tree(float p, float* lds) {
+    const int tid = threadIdx.x;
+    lds[tid] = p;
+    __syncthreads();
+    if (tid < 128) lds[tid] = lds[tid] + lds[tid + 128];
+    __syncthreads();
+    if (tid < 64) lds[tid] = lds[tid] + lds[tid + 64];
+    __syncthreads();
+    if (tid < 64) {
+        float v = lds[tid];
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) v = v + __shfl_down(v, d, 64);
+        if (tid == 0) lds[256] = v;
+    }
+    __syncthreads();
+    const float r = lds[256];
+    __syncthreads();
+    return r;
+}
+
+// Quantize one smoothed value with step d (rd = RN(1/d)).  In static mode the
+// dividend is first limited to +-128 d (exact scaling by a power of two), which
+// keeps the quotient finite and leaves every code unchanged: a quotient beyond
+// 127.5 saturates to +-127 either way.
+template <bool STATIC>
+__device__ __forceinline__ int quantize(float xh, float d, float rd) {
+    if (STATIC) {
+        const float lim = 128.0f * d;
+        xh = fminf(fmaxf(xh, -lim), lim);
+    }
+    return code_of(div_rn(xh, d, rd));
+}
+
+template <typename T, bool LN, bool STATIC, int CPT, bool CACHE_R>
+__global__ __launch_bounds__(1024) void act_quant_kernel(
+    const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
+    const float* __restrict__ gs, const float* __restrict__ bs, float eps,
+    const float* __restrict__ static_scale, int8_t* __restrict__ xq,
+    float* __restrict__ x_scale) {
+    __shared__ float lds[kLnThreads + 4];
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int64_t chunks = K / kChunk;
+    const float kf = static_cast<float>(K);
+
+    float rcp[CACHE_R ? CPT : 1][kChunk];
+    if (!LN && CACHE_R) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+            if (c < chunks) {
+                float sv[kChunk];
+                load_chunk(s, c, sv);
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) rcp[i][e] = 1.0f / sv[e];
+            }
+        }
+    }
+    float d_static = 0.0f, rd_static = 0.0f;
+    if (STATIC) {
+        d_static = *static_scale;
+        rd_static = 1.0f / d_static;
+    }
+
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        const T* row = x + m * K;
+        RawChunk<T> raw[CPT];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+            if (c < chunks) raw[i] = load_raw(row, c);
+        }
+        float v[CPT][kChunk];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) unpack(raw[i], v[i]);
+
+        if (LN) {
+            // mean: canonical sum of x
+            float p = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+                if (c < chunks) {
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) p = p + v[i][e];
+                }
+            }
+            const float mu = canonical_tree(p, lds) / kf;
+            // biased variance: canonical sum of RN(d*d)
+            p = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+                if (c < chunks) {
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) {
+                        v[i][e] = v[i][e] - mu;
+                        const float dd = v[i][e] * v[i][e];
+                        p = p + dd;
+                    }
+                }
+            }
+            const float var = canonical_tree(p, lds) / kf;
+            const float rho = 1.0f / __builtin_sqrtf(var + eps);
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+                if (c < chunks) {
+                    float g[kChunk], b[kChunk];
+                    load_chunk(gs, c, g);
+                    load_chunk(bs, c, b);
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) {
+                        float t = v[i][e] * rho;
+                        t = t * g[e];
+                        v[i][e] = t + b[e];
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+                if (c < chunks) {
+                    float sv[kChunk];
+                    load_chunk(s, c, sv);
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) {
+                        const float r = CACHE_R ? rcp[CACHE_R ? i : 0][e] : 1.0f / sv[e];
+                        v[i][e] = div_rn(v[i][e], sv[e], r);
+                    }
+                }
+            }
+        }
+
+        float d, rd;
+        if (STATIC) {
+            d = d_static;
+            rd = rd_static;
+        } else {
+            float mx = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+                if (c < chunks) {
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) mx = fmaxf(mx, fabsf(v[i][e]));
+                }
+            }
+            mx = block_max(mx, lds);
+            d = step_from_absmax(mx);
+            rd = 1.0f / d;
+            if (tid == 0) x_scale[m] = d;
+        }
+        int8_t* orow = xq + m * K;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+            if (c < chunks) {
+                int q[kChunk];
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[i][e], d, rd);
+                *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
+            }
+        }
+    }
+}
+
+// Any K: the row is re-read from memory for each sweep (mostly L2 hits).
+// 256 lanes, so LayerNorm partials are canonical here too.
+template <typename T, bool LN>
+__device__ __forceinline__ void smooth_chunk(const T* row, int64_t c, const float* s,
+                                             const float* gs, const float* bs, float mu,
+                                             float rho, float (&v)[kChunk]) {
+    load_chunk(row, c, v);
+    if (LN) {
+        float g[kChunk], b[kChunk];
+        load_chunk(gs, c, g);
+        load_chunk(bs, c, b);
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+            const float dlt = v[e] - mu;
+            float t = dlt * rho;
+            t = t * g[e];
+            v[e] = t + b[e];
+        }
+    } else {
+        float sv[kChunk];
+        load_chunk(s, c, sv);
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) v[e] = v[e] / sv[e];
+    }
+}
+
+template <typename T, bool LN, bool STATIC>
+__global__ __launch_bounds__(kLnThreads) void act_quant_stream_kernel(
+    const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
+    const float* __restrict__ gs, const float* __restrict__ bs, float eps,
+    const float* __restrict__ static_scale, int8_t* __restrict__ xq,
+    float* __restrict__ x_scale) {
+    __shared__ float lds[kLnThreads + 4];
+    const int tid = threadIdx.x;
+    const int64_t chunks = K / kChunk;
+    const float kf = static_cast<float>(K);
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        const T* row = x + m * K;
+        float mu = 0.0f, rho = 0.0f;
+        if (LN) {
+            float p = 0.0f;
+            for (int64_t c = tid; c < chunks; c += kLnThreads) {
+                float v[kChunk];
+                load_chunk(row, c, v);
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) p = p + v[e];
+            }
+            mu = canonical_tree(p, lds) / kf;
+            p = 0.0f;
+            for (int64_t c = tid; c < chunks; c += kLnThreads) {
+                float v[kChunk];
+                load_chunk(row, c, v);
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) {
+                    const float dlt = v[e] - mu;
+                    const float dd = dlt * dlt;
+                    p = p + dd;
+                }
+            }
+            const float var = canonical_tree(p, lds) / kf;
+            rho = 1.0f / __builtin_sqrtf(var + eps);
+        }
+        float d, rd;
+        if (STATIC) {
+            d = *static_scale;
+        } else {
+            float mx = 0.0f;
+            for (int64_t c = tid; c < chunks; c += kLnThreads) {
+                float v[kChunk];
+                smooth_chunk<T, LN>(row, c, s, gs, bs, mu, rho, v);
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) mx = fmaxf(mx, fabsf(v[e]));
+            }
+            mx = block_max(mx, lds);
+            d = step_from_absmax(mx);
+            if (tid == 0) x_scale[m] = d;
+        }
+        rd = 1.0f / d;
+        for (int64_t c = tid; c < chunks; c += kLnThreads) {
+            float v[kChunk];
+            smooth_chunk<T, LN>(row, c, s, gs, bs, mu, rho, v);
+            int q[kChunk];
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[e], d, rd);
+            *reinterpret_cast<uint2*>(xq + m * K + c * kChunk) = pack8(q);
+        }
+    }
+}
+
+struct ActArgs {
+    const void* x;
+    int64_t M, K;
+    const float *s, *gs, *bs;
+    float eps;
+    const float* static_scale;
+    int8_t* xq;
+    float* x_scale;
+};
+
+template <typename T, bool LN, bool STATIC, int CPT, bool CACHE_R>
+hipError_t run(const ActArgs& a, int threads, hipStream_t stream) {
+    const int64_t per_cu = std::max(1, 2048 / threads);
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.M, 256 * per_cu));
+    act_quant_kernel<T, LN, STATIC, CPT, CACHE_R><<<grid, threads, 0, stream>>>(
+        static_cast<const T*>(a.x), a.M, a.K, a.s, a.gs, a.bs, a.eps, a.static_scale, a.xq,
+        a.x_scale);
+    return hipGetLastError();
+}
+
+template <typename T, bool LN, bool STATIC>
+hipError_t run_stream(const ActArgs& a, hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.M, 2048));
+    act_quant_stream_kernel<T, LN, STATIC><<<grid, kLnThreads, 0, stream>>>(
+        static_cast<const T*>(a.x), a.M, a.K, a.s, a.gs, a.bs, a.eps, a.static_scale, a.xq,
+        a.x_scale);
+    return hipGetLastError();
+}
+
+int round_up64(int64_t v) { return static_cast<int>(((v + 63) / 64) * 64); }
+
+template <typename T, bool STATIC>
+hipError_t dispatch_plain(const ActArgs& a, hipStream_t stream) {
+    const int64_t chunks = a.K / kChunk;
+    int cpt = 1;
+    while (cpt <= 4 && (chunks + cpt - 1) / cpt > 512) cpt *= 2;
+    if (cpt > 4) {
+        cpt = 1;
+        while (cpt <= 8 && (chunks + cpt - 1) / cpt > 1024) cpt *= 2;
+    }
+    const int threads = std::max(64, round_up64((chunks + cpt - 1) / cpt));
+    switch (cpt) {
+        case 1: return run<T, false, STATIC, 1, true>(a, threads, stream);
+        case 2: return run<T, false, STATIC, 2, true>(a, threads, stream);
+        case 4: return run<T, false, STATIC, 4, true>(a, threads, stream);
+        case 8: return run<T, false, STATIC, 8, false>(a, threads, stream);
+        default: return run_stream<T, false, STATIC>(a, stream);
+    }
+}
+
+template <typename T, bool STATIC>
+hipError_t dispatch_ln(const ActArgs& a, hipStream_t stream) {
+    const int64_t chunks = a.K / kChunk;
+    const int64_t need = (chunks + kLnThreads - 1) / kLnThreads;
+    if (need <= 1) return run<T, true, STATIC, 1, false>(a, kLnThreads, stream);
+    if (need <= 2) return run<T, true, STATIC, 2, false>(a, kLnThreads, stream);
+    if (need <= 4) return run<T, true, STATIC, 4, false>(a, kLnThreads, stream);
+    if (need <= 8) return run<T, true, STATIC, 8, false>(a, kLnThreads, stream);
+    return run_stream<T, true, STATIC>(a, stream);
+}
+
+template <typename T>
+hipError_t dispatch(const ActArgs& a, bool ln, bool st, hipStream_t stream) {
+    if (ln) return st ? dispatch_ln<T, true>(a, stream) : dispatch_ln<T, false>(a, stream);
+    return st ? dispatch_plain<T, true>(a, stream) : dispatch_plain<T, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(const void* x, Dt x_dt, int64_t M, int64_t K, const float* s,
+                            const float* gamma_s, const float* beta_s, float eps,
+                            bool static_mode, const float* static_scale, int8_t* xq,
+                            float* x_scale, hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    const ActArgs a{x, M, K, s, gamma_s, beta_s, eps, static_scale, xq, x_scale};
+    const bool ln = (s == nullptr);
+    return (x_dt == Dt::BF16) ? dispatch<uint16_t>(a, ln, static_mode, stream)
+                              : dispatch<float>(a, ln, static_mode, stream);
+}
+
+}  // namespace sq

@@ -1,0 +1,126 @@
+// sq_device.hpp -- device-side helpers shared by the library's HIP kernels.
+//
+// Arithmetic rules (the library is built with -ffp-contract=off): every fp32
+// expression below is one IEEE operation rounded to nearest even, unless an
+// explicit fused multiply-add is written.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+constexpr float kFloor = 1e-7f;   // floor of every absolute maximum
+constexpr float kQmax = 127.0f;   // symmetric int8 code range [-127, 127]
+
+// Eight consecutive elements of a row, the unit of every vector load.
+constexpr int kChunk = 8;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Load the 8 elements of chunk c of a row as fp32 (bf16 widening is exact).
+template <typename T>
+__device__ __forceinline__ void load_chunk(const T* row, int64_t c, float (&v)[kChunk]);
+
+template <>
+__device__ __forceinline__ void load_chunk<uint16_t>(const uint16_t* row, int64_t c,
+                                                     float (&v)[kChunk]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + c * kChunk);
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+    v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+    v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+}
+
+template <>
+__device__ __forceinline__ void load_chunk<float>(const float* row, int64_t c,
+                                                  float (&v)[kChunk]) {
+    const float4 a = *reinterpret_cast<const float4*>(row + c * kChunk);
+    const float4 b = *reinterpret_cast<const float4*>(row + c * kChunk + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Raw 16-byte-granular chunk storage, so loads can be issued before use.
+template <typename T> struct RawChunk;
+template <> struct RawChunk<uint16_t> { uint4 u; };
+template <> struct RawChunk<float> { uint4 a, b; };
+
+template <typename T>
+__device__ __forceinline__ RawChunk<T> load_raw(const T* row, int64_t c);
+template <>
+__device__ __forceinline__ RawChunk<uint16_t> load_raw<uint16_t>(const uint16_t* row, int64_t c) {
+    return RawChunk<uint16_t>{*reinterpret_cast<const uint4*>(row + c * kChunk)};
+}
+template <>
+__device__ __forceinline__ RawChunk<float> load_raw<float>(const float* row, int64_t c) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + c * kChunk);
+    return RawChunk<float>{p[0], p[1]};
+}
+
+__device__ __forceinline__ void unpack(const RawChunk<uint16_t>& r, float* v) {
+    v[0] = bf16_lo(r.u.x); v[1] = bf16_hi(r.u.x);
+    v[2] = bf16_lo(r.u.y); v[3] = bf16_hi(r.u.y);
+    v[4] = bf16_lo(r.u.z); v[5] = bf16_hi(r.u.z);
+    v[6] = bf16_lo(r.u.w); v[7] = bf16_hi(r.u.w);
+}
+__device__ __forceinline__ void unpack(const RawChunk<float>& r, float* v) {
+    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+    v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+    v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+}
+
+// Correctly rounded quotient RN(a / b) for b > 0 normal, given rb = RN(1/b)
+// (computed with an IEEE division).  q0 = RN(a*rb) is within 1.5 ulp of a/b;
+// one residual step brings it within 1 ulp; by Markstein's theorem (residual
+// r = a - b*q exact, then RN(q + r*rb) with rb within half an ulp of 1/b) the
+// second step returns the correctly rounded quotient.  Valid whenever the
+// residuals do not underflow (|a/b| above ~2^-100) -- smaller quotients only
+// ever reach rne() as 0 or an absolute maximum below the floor -- and a/b
+// does not overflow.  Five VALU operations instead of the ten-instruction
+// IEEE division sequence.
+__device__ __forceinline__ float div_rn(float a, float b, float rb) {
+    float q = a * rb;
+    float r = __builtin_fmaf(-b, q, a);
+    q = __builtin_fmaf(r, rb, q);
+    r = __builtin_fmaf(-b, q, a);
+    return __builtin_fmaf(r, rb, q);
+}
+
+// Quantizer step from an absolute maximum: RN(max(FLOOR, m) / 127).
+__device__ __forceinline__ float step_from_absmax(float m) {
+    return fmaxf(m, kFloor) / kQmax;
+}
+
+// rne then clamp to [-127, 127], as an int.
+__device__ __forceinline__ int code_of(float q) {
+    float r = __builtin_rintf(q);
+    r = fminf(fmaxf(r, -kQmax), kQmax);
+    return static_cast<int>(r);
+}
+
+// Pack 8 codes into two 32-bit words (byte i = element i).
+__device__ __forceinline__ uint2 pack8(const int (&c)[kChunk]) {
+    uint32_t lo = (c[0] & 0xff) | ((c[1] & 0xff) << 8) | ((c[2] & 0xff) << 16) |
+                  (static_cast<uint32_t>(c[3]) << 24);
+    uint32_t hi = (c[4] & 0xff) | ((c[5] & 0xff) << 8) | ((c[6] & 0xff) << 16) |
+                  (static_cast<uint32_t>(c[7]) << 24);
+    return make_uint2(lo, hi);
+}
+
+// Wave-wide (64 lanes) maximum, result valid in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), d, 64)));
+    return v;
+}
+
+}  // namespace sq

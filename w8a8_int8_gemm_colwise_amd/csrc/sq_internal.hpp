@@ -1,0 +1,32 @@
+// sq_internal.hpp -- host-side launchers implemented by the library's HIP
+// translation units and called by the C ABI layer.  All sizes are validated
+// by the ABI layer before these run; each launcher only enqueues kernels and
+// returns the HIP error of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+// Calibration (offline half).
+hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w, Dt w_dt,
+                            int64_t N, int64_t K, float alpha, const float* gamma,
+                            const float* beta, float* s, int8_t* wq, float* w_scale,
+                            float* act_scale_static, float* gamma_s, float* beta_s,
+                            float* x_absmax, float* w_absmax, hipStream_t stream);
+
+// Activation smoothing + quantization (runtime).
+hipError_t launch_act_quant(const void* x, Dt x_dt, int64_t M, int64_t K, const float* s,
+                            const float* gamma_s, const float* beta_s, float eps,
+                            bool static_mode, const float* static_scale, int8_t* xq,
+                            float* x_scale, hipStream_t stream);
+
+// Int8 GEMM with dequantizing epilogue.  out_kind: 0 = f32, 1 = bf16, 2 = i32.
+hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
+                       const int8_t* wq, const float* w_scale, int64_t M, int64_t N, int64_t K,
+                       void* y, int out_kind, hipStream_t stream);
+
+}  // namespace sq
