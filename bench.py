@@ -102,7 +102,7 @@ def main():
     ap.add_argument("--workload", default="opt6.7b", choices=sorted(WORKLOADS))
     ap.add_argument("--decode-m", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
