@@ -72,6 +72,18 @@ def test_ragged_every_element(case):
     run_layer(spec, xc, w, x, mode, gamma=g, beta=b)
 
 
+@pytest.mark.parametrize("shape", [(1100, 13000, 256), (777, 3000, 1280), (2049, 4097, 512)],
+                         ids=lambda t: "x".join(map(str, t)))
+def test_ragged_large_tiles_sampled(shape):
+    """Shapes that select the large-tile kernels with ragged edges in M and N;
+    sampled rows always include the first and last token, sampled columns the
+    first and last output channel."""
+    M, N, K = shape
+    spec = datagen.random_layer(M, N, K, seed=M + N + K, n_outliers=4, T=64)
+    xc, w, x = _inputs(spec)
+    run_layer(spec, xc, w, x, "per_token", n_rows=40, n_cols=48, seed=M)
+
+
 # ---- full-size workloads: sampled elements ---------------------------------------
 
 @pytest.mark.parametrize("l", range(4), ids=["qkv", "out_proj", "fc1", "fc2"])

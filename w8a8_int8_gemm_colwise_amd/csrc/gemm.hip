@@ -15,9 +15,11 @@
 // while the matrix cores work on tile k).  Each wave owns a WM x WN sub-tile
 // made of 32x32 v_mfma_i32_32x32x32_i8 tiles accumulated in int32 registers.
 // LDS rows are 64 bytes; the 16-byte chunk c of row r is stored at chunk
-// c ^ f(r) so that the ds_read_b128 of 16 consecutive rows hit distinct banks.
+// c ^ swz(r) so that the operand fetches (ds_read_b128) hit distinct banks.
 // Blocks are remapped so that the tiles one XCD runs are neighbours (sharing
 // A rows and B columns in that XCD's L2).
+#include <type_traits>
+
 #include "sq_device.hpp"
 #include "sq_internal.hpp"
 
@@ -31,10 +33,27 @@ constexpr int kBK = 64;              // K bytes per LDS stage
 constexpr int kChunksPerRow = kBK / 16;
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// 16-byte chunk permutation of a 64-byte LDS row.  Chosen by measurement on
+// gfx950 (SQ_LDS_BANK_CONFLICT): for the MFMA operand fetch -- lanes 0-31
+// read 32 consecutive rows at one chunk, lanes 32-63 the next chunk -- this
+// permutation is free of bank conflicts, while e.g. c ^ (row & 3) or
+// c ^ ((row >> 1 ^ row >> 3) & 3) serialize every ds_read_b128 two or four ways.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * kBK + ((chunk ^ swz(row)) << 4);
+}
+
+// Rows of BK bytes (64 or 128).  128-byte rows use c ^ ((row >> 1) & 7),
+// likewise measured conflict-free for the operand fetch pattern.
+template <int BK>
+__device__ __forceinline__ int swz_k(int row) {
+    static_assert(BK == 64 || BK == 128, "64- or 128-byte rows");
+    return BK == 64 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
+template <int BK>
+__device__ __forceinline__ int lds_off_k(int row, int chunk) {
+    return row * BK + ((chunk ^ swz_k<BK>(row)) << 4);
 }
 
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2 };
@@ -49,8 +68,6 @@ struct Tile {
     static constexpr int LA = BM * kChunksPerRow / kThreads;  // A chunks per thread
     static constexpr int LB = BN * kChunksPerRow / kThreads;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
-    static_assert(LA * kThreads == BM * kChunksPerRow, "A tile divides over threads");
-    static_assert(LB * kThreads == BN * kChunksPerRow, "B tile divides over threads");
 };
 
 // Map the launch index to (tile_m, tile_n): undo the round-robin XCD dispatch
@@ -71,11 +88,56 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
     tn = in_g / gm;
 }
 
+// Dequantizing epilogue for a wave's TM x TN grid of 32x32 accumulator tiles
+// whose top-left output element is (row0, col0).  In a 32x32 MFMA result,
+// lane l holds rows 8*g + 4*(l/32) + r (g, r in 0..3) of column l%32.
+// y = RN(RN_f32(acc) * RN(dx_row * dw_col)); bf16 output rounds that to
+// nearest even; the int32 output stores acc.
+template <int OUT, int TM, int TN>
+__device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int row0, int col0, int lane,
+                                           const float* __restrict__ sx, int sx_per_token,
+                                           const float* __restrict__ sw, void* __restrict__ Y,
+                                           int M, int N) {
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = row0 + i * 32 + 8 * g + 4 * fhalf + r;
+                if (row >= M) continue;
+                const float dx = (OUT == kOutI32) ? 0.0f : sx[sx_per_token ? row : 0];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = col0 + j * 32 + frow;
+                    if (col >= N) continue;
+                    const int a = acc[i][j][4 * g + r];
+                    const int64_t o = static_cast<int64_t>(row) * N + col;
+                    if (OUT == kOutI32) {
+                        static_cast<int32_t*>(Y)[o] = a;
+                    } else {
+                        const float f = dx * sw[col];
+                        const float y = static_cast<float>(a) * f;
+                        if (OUT == kOutF32)
+                            static_cast<float*>(Y)[o] = y;
+                        else
+                            static_cast<__bf16*>(Y)[o] = static_cast<__bf16>(y);
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
+    static_assert(T::LA * T::kThreads == BM * kChunksPerRow, "A tile divides over threads");
+    static_assert(T::LB * T::kThreads == BN * kChunksPerRow, "B tile divides over threads");
     __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kBK];
     __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * kBK];
 
@@ -93,7 +155,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     // global -> register staging descriptors
     const int8_t* a_src[T::LA];
     const int8_t* b_src[T::LB];
-    int a_lds[T::LA], b_lds[T::LB], a_kc[T::LA], b_kc[T::LB];
+    int a_lds[T::LA], b_lds[T::LB];
 #pragma unroll
     for (int j = 0; j < T::LA; ++j) {
         const int q = tid + j * T::kThreads;
@@ -101,7 +163,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
         const int grow = min(m0 + row, M - 1);
         a_src[j] = A + static_cast<int64_t>(grow) * K + c * 16;
         a_lds[j] = lds_off(row, c);
-        a_kc[j] = c * 16;
     }
 #pragma unroll
     for (int j = 0; j < T::LB; ++j) {
@@ -110,17 +171,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
         const int grow = min(n0 + row, N - 1);
         b_src[j] = B + static_cast<int64_t>(grow) * K + c * 16;
         b_lds[j] = lds_off(row, c);
-        b_kc[j] = c * 16;
     }
 
     v4i ra[T::LA], rb[T::LB];
     auto gload = [&](int k0) {
 #pragma unroll
         for (int j = 0; j < T::LA; ++j)
-            ra[j] = (k0 + a_kc[j] < K) ? *reinterpret_cast<const v4i*>(a_src[j] + k0) : v4i{0, 0, 0, 0};
+            ra[j] = *reinterpret_cast<const v4i*>(a_src[j] + k0);
 #pragma unroll
         for (int j = 0; j < T::LB; ++j)
-            rb[j] = (k0 + b_kc[j] < K) ? *reinterpret_cast<const v4i*>(b_src[j] + k0) : v4i{0, 0, 0, 0};
+            rb[j] = *reinterpret_cast<const v4i*>(b_src[j] + k0);
     };
     auto sstore = [&](int buf) {
 #pragma unroll
@@ -173,37 +233,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
         __syncthreads();
     }
 
-    // epilogue: lane holds rows 8*g + 4*(lane/32) + r (g, r in 0..3) of
-    // column lane%32 of each 32x32 tile
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * T::WM + i * 32 + 8 * g + 4 * fhalf + r;
-                if (row >= M) continue;
-                const float dx = (OUT == kOutI32) ? 0.0f : sx[sx_per_token ? row : 0];
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j) {
-                    const int col = n0 + wn * T::WN + j * 32 + frow;
-                    if (col >= N) continue;
-                    const int a = acc[i][j][4 * g + r];
-                    const int64_t o = static_cast<int64_t>(row) * N + col;
-                    if (OUT == kOutI32) {
-                        static_cast<int32_t*>(Y)[o] = a;
-                    } else {
-                        const float f = dx * sw[col];
-                        const float y = static_cast<float>(a) * f;
-                        if (OUT == kOutF32)
-                            static_cast<float*>(Y)[o] = y;
-                        else
-                            static_cast<__bf16*>(Y)[o] = static_cast<__bf16>(y);
-                    }
-                }
-            }
-        }
-    }
+    store_tile<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + wn * T::WN, lane, sx, sx_per_token,
+                                  sw, Y, M, N);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -230,6 +261,206 @@ hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* 
     return hipGetLastError();
 }
 
+// ---- pipelined kernel: direct global->LDS loads, STAGES LDS stages -----------
+//
+// Each stage holds the A rows then the B rows of one BK-byte K slice (rows of
+// BK bytes, 16-byte chunks permuted by swz_k).  A stage is filled with
+// global_load_lds_dwordx4: one instruction moves 64 lanes x 16 bytes into 1 KB
+// of consecutive LDS, so lane q of a transfer fetches the global chunk whose
+// swizzled LDS slot is q.  No VGPRs hold tiles in flight, so STAGES-1 stages
+// are in flight while the matrix cores work on another.  The stages are
+// distinct LDS arrays so the compiler can see that reading one stage does not
+// depend on the transfers into the others; the waits are explicit vmcnt
+// counts followed by a plain s_barrier, fenced for both the IR optimizers and
+// the machine scheduler.
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Ordering point for both the IR optimizers (memory clobber) and the machine
+// scheduler (sched_barrier with an empty mask lets nothing cross it).
+__device__ __forceinline__ void compiler_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MIN_BLOCKS, int OUT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) void gemm_pipe_kernel(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
+    int sx_per_token, const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    using T = Tile<BM, BN, WAVES_M, WAVES_N>;
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int kRows = BM + BN;
+    constexpr int kStageBytes = kRows * BK;
+    constexpr int kCPR = BK / 16;              // 16-byte chunks per row
+    constexpr int kRowsPerXfer = 1024 / BK;    // 1 KB per wave-wide transfer
+    constexpr int kIssues = kRows / kRowsPerXfer;
+    constexpr int IPW = kIssues / NW;
+    static_assert(IPW * NW == kIssues, "stage divides over the waves");
+    static_assert(BM % kRowsPerXfer == 0, "a transfer never straddles A and B");
+    static_assert(STAGES >= 3 && STAGES <= 4, "3 or 4 stages");
+    __shared__ __attribute__((aligned(1024))) int8_t L0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) int8_t L1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) int8_t L2[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) int8_t L3[STAGES > 3 ? kStageBytes : 16];
+
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    int tmi, tni;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+    // byte offset (from A or B) of the source chunk of every transfer this
+    // lane takes part in; the caller guarantees M*K and N*K fit in int32
+    int src_off[IPW];
+    bool src_a[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int q = (wave * IPW + i) * 64 + lane;  // 16-byte slot within the stage
+        const int row = q / kCPR;
+        const int c = (q % kCPR) ^ swz_k<BK>(row);
+        src_a[i] = row < BM;  // uniform per transfer: BM is a multiple of 16
+        src_off[i] = src_a[i] ? min(m0 + row, M - 1) * K + c * 16
+                              : min(n0 + row - BM, N - 1) * K + c * 16;
+    }
+    auto issue = [&](int8_t* stage, int k0) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int8_t* g = (src_a[i] ? A : B) + (src_off[i] + k0);
+            __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(stage + (wave * IPW + i) * 1024), 16, 0, 0);
+        }
+    };
+
+    v16i acc[T::TM][T::TN];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+    auto compute = [&](const int8_t* S) {
+#pragma unroll
+        for (int kk = 0; kk < BK / 32; ++kk) {
+            v4i fa[T::TM], fb[T::TN];
+            const int chunk = 2 * kk + fhalf;
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+                fa[i] = *reinterpret_cast<const v4i*>(
+                    S + lds_off_k<BK>(wm * T::WM + i * 32 + frow, chunk));
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+                fb[j] = *reinterpret_cast<const v4i*>(
+                    S + BM * BK + lds_off_k<BK>(wn * T::WN + j * 32 + frow, chunk));
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // Wait until this wave's transfers into the stage about to be read have
+    // landed (`younger` later stages may stay in flight), then meet the other
+    // waves: after the barrier every wave's part of the stage is in LDS and
+    // every wave has finished reading the stage that the next issue reuses.
+    auto sync_stage = [&](int younger) {
+        if (younger >= 2) wait_vmcnt<2 * IPW>();
+        else if (younger == 1) wait_vmcnt<IPW>();
+        else wait_vmcnt<0>();
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+    };
+    // One pipeline step for stage t held in `cur`; the step then refills
+    // `nxt` (the buffer read one step earlier) with stage t + STAGES - 1.  In
+    // the steady state STAGES-2 younger stages are in flight and the refill is
+    // unconditional, so the step is straight-line code.  The buffers are passed
+    // as the LDS arrays themselves so the compiler keeps their identities.
+    const int KT = K / BK;
+    auto steady = [&](int t, const int8_t* cur, int8_t* nxt) {
+        wait_vmcnt<(STAGES - 2) * IPW>();
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        issue(nxt, (t + STAGES - 1) * BK);
+        compute(cur);
+    };
+    auto drain = [&](int t, const int8_t* cur, int8_t* nxt) {
+        sync_stage(min(KT - 1 - t, STAGES - 2));
+        if (t + STAGES - 1 < KT) issue(nxt, (t + STAGES - 1) * BK);
+        compute(cur);
+    };
+
+    issue(L0, 0);
+    if (KT > 1) issue(L1, BK);
+    if (STAGES > 3 && KT > 2) issue(L2, 2 * BK);
+    // steady state in groups of STAGES steps (buffers rotate 0..STAGES-1)
+    int t = 0;
+    if constexpr (STAGES == 4) {
+        for (; t + 2 * STAGES - 1 <= KT; t += STAGES) {
+            steady(t, L0, L3);
+            steady(t + 1, L1, L0);
+            steady(t + 2, L2, L1);
+            steady(t + 3, L3, L2);
+        }
+        for (int g = 0; g < 2; ++g, t += STAGES) {
+            if (t < KT) drain(t, L0, L3);
+            if (t + 1 < KT) drain(t + 1, L1, L0);
+            if (t + 2 < KT) drain(t + 2, L2, L1);
+            if (t + 3 < KT) drain(t + 3, L3, L2);
+        }
+    } else {
+        for (; t + 2 * STAGES - 1 <= KT; t += STAGES) {
+            steady(t, L0, L2);
+            steady(t + 1, L1, L0);
+            steady(t + 2, L2, L1);
+        }
+        for (int g = 0; g < 2; ++g, t += STAGES) {
+            if (t < KT) drain(t, L0, L2);
+            if (t + 1 < KT) drain(t + 1, L1, L0);
+            if (t + 2 < KT) drain(t + 2, L2, L1);
+        }
+    }
+
+    store_tile<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + wn * T::WN, lane, sx, sx_per_token,
+                                  sw, Y, M, N);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MIN_BLOCKS>
+hipError_t run_pipe(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
+                    const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const dim3 grid(tiles), block(64 * WAVES_M * WAVES_N);
+    const int pt = per_token ? 1 : 0;
+    switch (out) {
+        case kOutF32:
+            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutF32>
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            break;
+        case kOutBF16:
+            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutBF16>
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            break;
+        default:
+            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutI32>
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
@@ -239,6 +470,21 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     if (M <= 64)
         return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
+    // pipelined kernels: 128-byte K stages, operand offsets in int32
+    const bool pipe_ok = (K % 128 == 0) && M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
+    if (pipe_ok) {
+        // pick the tile by whole waves of 256 CUs: a 256x256 tile does twice the
+        // work of a 256x128 tile at slightly higher efficiency
+        const int64_t t_big = ((M + 255) / 256) * ((N + 255) / 256);
+        const int64_t t_mid = ((M + 255) / 256) * ((N + 127) / 128);
+        const int64_t cost_big = ((t_big + 255) / 256) * 2 * 100;
+        const int64_t cost_mid = ((t_mid + 255) / 256) * 105;
+        if (cost_big <= cost_mid)
+            return run_pipe<256, 256, 2, 4, 64, 4, 1>(xq, x_scale, x_per_token, wq, w_scale, m, n, k,
+                                                      y, out_kind, stream);
+        return run_pipe<256, 128, 4, 2, 128, 3, 1>(xq, x_scale, x_per_token, wq, w_scale, m, n, k,
+                                                   y, out_kind, stream);
+    }
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 127) / 128);
     if (big_tiles >= 256)
         return run<256, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
