@@ -31,6 +31,7 @@ constexpr int kLnThreads = 256;
 __device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
     const int nw = blockDim.x >> 6;
+    if (nw == 1) return v;
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     float m = red[0];
@@ -74,8 +75,14 @@ __device__ __forceinline__ int quantize(float xh, float d, float rd) {
     return code_of(div_rn(xh, d, rd));
 }
 
-template <typename T, bool LN, bool STATIC, int CPT, bool CACHE_R>
-__global__ __launch_bounds__(1024) void act_quant_kernel(
+// D > 0: the lane's per-column constants (s_k and RN(1/s_k) in plain mode,
+// gamma'_k and beta'_k in LayerNorm mode) are loaded once per block and kept in
+// registers, and the loads of the block's next D rows are in flight while the
+// current row is reduced and quantized (a ring of D+1 rows of 16-byte chunks).
+// D = 0: the constants are re-read per row (L2 hits), 1/s_k is an IEEE
+// division, and nothing is prefetched.
+template <typename T, bool LN, bool STATIC, int CPT, int D, int MAXT>
+__global__ __launch_bounds__(MAXT) void act_quant_kernel(
     const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
     const float* __restrict__ gs, const float* __restrict__ bs, float eps,
     const float* __restrict__ static_scale, int8_t* __restrict__ xq,
@@ -85,17 +92,39 @@ __global__ __launch_bounds__(1024) void act_quant_kernel(
     const int nthr = blockDim.x;
     const int64_t chunks = K / kChunk;
     const float kf = static_cast<float>(K);
+    constexpr bool CACHE = D > 0;
+    constexpr int CC = CACHE ? CPT : 1;
+    const int64_t G = gridDim.x;
 
-    float rcp[CACHE_R ? CPT : 1][kChunk];
-    if (!LN && CACHE_R) {
+    RawChunk<T> ring[D + 1][CPT];
+    auto fetch = [&](int64_t m, RawChunk<T> (&r)[CPT]) {
+        const T* row = x + m * K;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int64_t c = tid + static_cast<int64_t>(i) * nthr;
-            if (c < chunks) {
-                float sv[kChunk];
-                load_chunk(s, c, sv);
+            if (c < chunks) r[i] = load_raw(row, c);
+        }
+    };
+    // the first rows' loads go out before the per-column set-up below
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) rcp[i][e] = 1.0f / sv[e];
+    for (int j = 0; j < D; ++j)
+        if (blockIdx.x + j * G < M) fetch(blockIdx.x + j * G, ring[j]);
+
+    // per-column constants: c0 = s (plain) or gamma' (LN); c1 = 1/s or beta'
+    float c0[CC][kChunk], c1[CC][kChunk];
+    if (CACHE) {
+#pragma unroll
+        for (int i = 0; i < CC; ++i) {
+            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+            if (c < chunks) {
+                if (LN) {
+                    load_chunk(gs, c, c0[i]);
+                    load_chunk(bs, c, c1[i]);
+                } else {
+                    load_chunk(s, c, c0[i]);
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) c1[i][e] = 1.0f / c0[i][e];
+                }
             }
         }
     }
@@ -104,18 +133,11 @@ __global__ __launch_bounds__(1024) void act_quant_kernel(
         d_static = *static_scale;
         rd_static = 1.0f / d_static;
     }
-
-    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
-        const T* row = x + m * K;
-        RawChunk<T> raw[CPT];
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
-            if (c < chunks) raw[i] = load_raw(row, c);
-        }
+    for (int64_t m = blockIdx.x; m < M; m += G) {
+        if (m + D * G < M) fetch(m + D * G, ring[D]);
         float v[CPT][kChunk];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) unpack(raw[i], v[i]);
+        for (int i = 0; i < CPT; ++i) unpack(ring[0][i], v[i]);
 
         if (LN) {
             // mean: canonical sum of x
@@ -150,8 +172,16 @@ __global__ __launch_bounds__(1024) void act_quant_kernel(
                 const int64_t c = tid + static_cast<int64_t>(i) * nthr;
                 if (c < chunks) {
                     float g[kChunk], b[kChunk];
-                    load_chunk(gs, c, g);
-                    load_chunk(bs, c, b);
+                    if (CACHE) {
+#pragma unroll
+                        for (int e = 0; e < kChunk; ++e) {
+                            g[e] = c0[CACHE ? i : 0][e];
+                            b[e] = c1[CACHE ? i : 0][e];
+                        }
+                    } else {
+                        load_chunk(gs, c, g);
+                        load_chunk(bs, c, b);
+                    }
 #pragma unroll
                     for (int e = 0; e < kChunk; ++e) {
                         float t = v[i][e] * rho;
@@ -165,12 +195,15 @@ __global__ __launch_bounds__(1024) void act_quant_kernel(
             for (int i = 0; i < CPT; ++i) {
                 const int64_t c = tid + static_cast<int64_t>(i) * nthr;
                 if (c < chunks) {
-                    float sv[kChunk];
-                    load_chunk(s, c, sv);
+                    if (CACHE) {
 #pragma unroll
-                    for (int e = 0; e < kChunk; ++e) {
-                        const float r = CACHE_R ? rcp[CACHE_R ? i : 0][e] : 1.0f / sv[e];
-                        v[i][e] = div_rn(v[i][e], sv[e], r);
+                        for (int e = 0; e < kChunk; ++e)
+                            v[i][e] = div_rn(v[i][e], c0[CACHE ? i : 0][e], c1[CACHE ? i : 0][e]);
+                    } else {
+                        float sv[kChunk];
+                        load_chunk(s, c, sv);
+#pragma unroll
+                        for (int e = 0; e < kChunk; ++e) v[i][e] = div_rn(v[i][e], sv[e], 1.0f / sv[e]);
                     }
                 }
             }
@@ -206,6 +239,10 @@ __global__ __launch_bounds__(1024) void act_quant_kernel(
                 *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
             }
         }
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) ring[j][i] = ring[j + 1][i];
     }
 }
 
@@ -308,11 +345,12 @@ struct ActArgs {
     float* x_scale;
 };
 
-template <typename T, bool LN, bool STATIC, int CPT, bool CACHE_R>
+template <typename T, bool LN, bool STATIC, int CPT, int D, int MAXT = 1024>
 hipError_t run(const ActArgs& a, int threads, hipStream_t stream) {
-    const int64_t per_cu = std::max(1, 2048 / threads);
+    // resident blocks: about 16 waves per CU, each block walks several rows
+    const int64_t per_cu = std::max(1, 1024 / threads);
     const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.M, 256 * per_cu));
-    act_quant_kernel<T, LN, STATIC, CPT, CACHE_R><<<grid, threads, 0, stream>>>(
+    act_quant_kernel<T, LN, STATIC, CPT, D, MAXT><<<grid, threads, 0, stream>>>(
         static_cast<const T*>(a.x), a.M, a.K, a.s, a.gs, a.bs, a.eps, a.static_scale, a.xq,
         a.x_scale);
     return hipGetLastError();
@@ -327,35 +365,31 @@ hipError_t run_stream(const ActArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-int round_up64(int64_t v) { return static_cast<int>(((v + 63) / 64) * 64); }
 
 template <typename T, bool STATIC>
 hipError_t dispatch_plain(const ActArgs& a, hipStream_t stream) {
     const int64_t chunks = a.K / kChunk;
-    int cpt = 1;
-    while (cpt <= 4 && (chunks + cpt - 1) / cpt > 512) cpt *= 2;
-    if (cpt > 4) {
-        cpt = 1;
-        while (cpt <= 8 && (chunks + cpt - 1) / cpt > 1024) cpt *= 2;
-    }
-    const int threads = std::max(64, round_up64((chunks + cpt - 1) / cpt));
-    switch (cpt) {
-        case 1: return run<T, false, STATIC, 1, true>(a, threads, stream);
-        case 2: return run<T, false, STATIC, 2, true>(a, threads, stream);
-        case 4: return run<T, false, STATIC, 4, true>(a, threads, stream);
-        case 8: return run<T, false, STATIC, 8, false>(a, threads, stream);
-        default: return run_stream<T, false, STATIC>(a, stream);
-    }
+    // rows up to 2048 chunks: one or two 16-byte loads per lane and row with the
+    // per-column constants cached and the next row prefetched (measured: one
+    // prefetched row beats deeper rings on the MI355X); longer rows:
+    // four (up to 1024 lanes) or eight (up to 768 lanes) loads per lane without
+    // caching; past that the multi-sweep kernel
+    if (chunks <= 64) return run<T, false, STATIC, 1, 1>(a, 64, stream);
+    if (chunks <= 2048) return run<T, false, STATIC, 2, 1>(a, round_up64((chunks + 1) / 2), stream);
+    if (chunks <= 4 * 1024) return run<T, false, STATIC, 4, 0>(a, round_up64((chunks + 3) / 4), stream);
+    if (chunks <= 8 * 768)
+        return run<T, false, STATIC, 8, 0, 768>(a, round_up64((chunks + 7) / 8), stream);
+    return run_stream<T, false, STATIC>(a, stream);
 }
 
 template <typename T, bool STATIC>
 hipError_t dispatch_ln(const ActArgs& a, hipStream_t stream) {
     const int64_t chunks = a.K / kChunk;
     const int64_t need = (chunks + kLnThreads - 1) / kLnThreads;
-    if (need <= 1) return run<T, true, STATIC, 1, false>(a, kLnThreads, stream);
-    if (need <= 2) return run<T, true, STATIC, 2, false>(a, kLnThreads, stream);
-    if (need <= 4) return run<T, true, STATIC, 4, false>(a, kLnThreads, stream);
-    if (need <= 8) return run<T, true, STATIC, 8, false>(a, kLnThreads, stream);
+    if (need <= 1) return run<T, true, STATIC, 1, 1, kLnThreads>(a, kLnThreads, stream);
+    if (need <= 2) return run<T, true, STATIC, 2, 1, kLnThreads>(a, kLnThreads, stream);
+    if (need <= 4) return run<T, true, STATIC, 4, 1, kLnThreads>(a, kLnThreads, stream);
+    if (need <= 8) return run<T, true, STATIC, 8, 0, kLnThreads>(a, kLnThreads, stream);
     return run_stream<T, true, STATIC>(a, stream);
 }
 

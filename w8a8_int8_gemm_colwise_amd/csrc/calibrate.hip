@@ -11,12 +11,14 @@
 //   dequantize after the contraction).
 //
 // Kernels (all HBM-streaming except the O(K) factor pass):
-//   fill_maxima     a_j = w_j = FLOOR bits, static scale bits = 0
-//   colmax          column |max| of a row-major [rows, K] tensor: 16-byte
-//                   loads along K, rows split over the waves of a block and over
-//                   blocks, per-block LDS combine, one uint atomicMax per column
-//                   per block (non-negative floats order like their bits)
-//   smooth_factor   s_j (fp64 pow, one rounding), gamma/beta fold, static scale
+//   colmax_partial  column |max| of X_cal and of W in one launch: 16-byte loads
+//                   along K, rows split over the waves of a block and over
+//                   blocks, per-block LDS combine, per-block maxima written to
+//                   scratch rows (non-negative floats order like their bits)
+//   smooth_factor   reduce the per-block maxima to a_j, w_j; s_j (fp64 pow, one
+//                   rounding), gamma/beta fold, static scale
+//   (fallback when the scratch does not fit: fill_maxima + colmax with one
+//   uint atomicMax per column per block)
 //   weight_quant    per output row: What = W*s, row |max|, dw_n, codes; the row
 //                   stays in registers between the max and the quantize passes
 #include <algorithm>
@@ -42,7 +44,7 @@ __global__ void fill_maxima_kernel(uint32_t* __restrict__ xa, uint32_t* __restri
 
 // ---- column absmax ----------------------------------------------------------
 
-constexpr int kColmaxThreads = 512;  // 8 waves; each wave walks its own rows
+constexpr int kColmaxThreads = 1024;  // 16 waves; each wave walks its own rows
 constexpr int kColmaxWaves = kColmaxThreads / 64;
 
 template <typename T>
@@ -86,37 +88,45 @@ struct ColmaxLane<float> {
     __device__ uint32_t f32_bits(int i) const { return m[i]; }
 };
 
+// Column |max| of rows [r_begin, r_end) of a row-major [rows, K] tensor over
+// the kSeg columns of segment `seg`, combined over the block's waves in LDS.
+// The block's result for column c is left in red[0][c] (as fp32 bit patterns,
+// which order like the values since they are non-negative).
 template <typename T>
-__global__ __launch_bounds__(kColmaxThreads) void colmax_kernel(
-    const T* __restrict__ x, int64_t rows, int64_t K, int64_t rows_per_block,
-    uint32_t* __restrict__ out_bits) {
+__device__ __forceinline__ void colmax_block(const T* __restrict__ x, int64_t K, int64_t seg,
+                                             int64_t r_begin, int64_t r_end,
+                                             uint32_t (*red)[64 * ColmaxLane<uint16_t>::kCols]) {
     using Lane = ColmaxLane<T>;
     constexpr int kSeg = 64 * Lane::kCols;  // columns covered by one block
-    __shared__ uint32_t red[kColmaxWaves][kSeg];
-
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t col = static_cast<int64_t>(blockIdx.x) * kSeg + lane * Lane::kCols;
-    const int64_t r_begin = static_cast<int64_t>(blockIdx.y) * rows_per_block;
-    const int64_t r_end = min(rows, r_begin + rows_per_block);
+    const int64_t col = seg * kSeg + lane * Lane::kCols;
 
     Lane acc;
     acc.init();
     if (col < K) {
         const T* p = x + col;
         int64_t r = r_begin + wave;
-        // four independent 16-byte loads in flight per lane
-        for (; r + 3 * kColmaxWaves < r_end; r += 4 * kColmaxWaves) {
-            const uint4 u0 = *reinterpret_cast<const uint4*>(p + r * K);
-            const uint4 u1 = *reinterpret_cast<const uint4*>(p + (r + kColmaxWaves) * K);
-            const uint4 u2 = *reinterpret_cast<const uint4*>(p + (r + 2 * kColmaxWaves) * K);
-            const uint4 u3 = *reinterpret_cast<const uint4*>(p + (r + 3 * kColmaxWaves) * K);
-            acc.add(u0);
-            acc.add(u1);
-            acc.add(u2);
-            acc.add(u3);
+        // batches of eight 16-byte loads per lane; the next batch is issued
+        // before the current one is folded in (two batches in flight)
+        constexpr int U = 8;
+        constexpr int64_t kStep = U * kColmaxWaves;
+        uint4 cur[U], nxt[U];
+        auto load_batch = [&](int64_t r0, uint4 (&u)[U]) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const int64_t rr = r0 + j * kColmaxWaves;
+                u[j] = (rr < r_end) ? *reinterpret_cast<const uint4*>(p + rr * K) : make_uint4(0, 0, 0, 0);
+            }
+        };
+        if (r < r_end) load_batch(r, cur);
+        for (; r < r_end; r += kStep) {
+            if (r + kStep < r_end) load_batch(r + kStep, nxt);
+#pragma unroll
+            for (int j = 0; j < U; ++j) acc.add(cur[j]);
+#pragma unroll
+            for (int j = 0; j < U; ++j) cur[j] = nxt[j];
         }
-        for (; r < r_end; r += kColmaxWaves) acc.add(*reinterpret_cast<const uint4*>(p + r * K));
     }
 #pragma unroll
     for (int i = 0; i < Lane::kCols; ++i) red[wave][lane * Lane::kCols + i] = acc.f32_bits(i);
@@ -125,8 +135,58 @@ __global__ __launch_bounds__(kColmaxThreads) void colmax_kernel(
         uint32_t v = red[0][c];
 #pragma unroll
         for (int w = 1; w < kColmaxWaves; ++w) v = max(v, red[w][c]);
+        red[0][c] = v;
+    }
+    __syncthreads();
+}
+
+// Atomic variant: fold the block's maxima into out_bits (pre-filled with the
+// floor) with one uint atomicMax per column.
+template <typename T>
+__global__ __launch_bounds__(kColmaxThreads) void colmax_kernel(
+    const T* __restrict__ x, int64_t rows, int64_t K, int64_t rows_per_block,
+    uint32_t* __restrict__ out_bits) {
+    constexpr int kSeg = 64 * ColmaxLane<T>::kCols;
+    __shared__ uint32_t red[kColmaxWaves][64 * ColmaxLane<uint16_t>::kCols];
+    const int64_t r_begin = static_cast<int64_t>(blockIdx.y) * rows_per_block;
+    const int64_t r_end = min(rows, r_begin + rows_per_block);
+    colmax_block<T>(x, K, blockIdx.x, r_begin, r_end, red);
+    for (int c = threadIdx.x; c < kSeg; c += kColmaxThreads) {
         const int64_t gc = static_cast<int64_t>(blockIdx.x) * kSeg + c;
-        if (gc < K && v > kFloorBits) atomicMax(out_bits + gc, v);
+        if (gc < K && red[0][c] > kFloorBits) atomicMax(out_bits + gc, red[0][c]);
+    }
+}
+
+// Partial variant, X_cal and W in one launch: blocks [0, segs_x*splits_x) cover
+// X_cal, the rest W; block (seg, split) writes its column maxima to row `split`
+// of `partial` ([splits_x + splits_w, K] words), which the factor kernel
+// reduces.  No fill and no atomics; block 0 also clears the static-scale word.
+template <typename TX, typename TW>
+__global__ __launch_bounds__(kColmaxThreads) void colmax_partial_kernel(
+    const TX* __restrict__ x, int64_t T, const TW* __restrict__ w, int64_t N, int64_t K,
+    int segs_x, int64_t rpb_x, int segs_w, int64_t rpb_w, int splits_x,
+    uint32_t* __restrict__ partial, uint32_t* __restrict__ static_bits) {
+    __shared__ uint32_t red[kColmaxWaves][64 * ColmaxLane<uint16_t>::kCols];
+    if (blockIdx.x == 0 && threadIdx.x == 0 && static_bits) *static_bits = 0u;
+    int64_t b = blockIdx.x;
+    const int64_t nbx = static_cast<int64_t>(segs_x) * splits_x;
+    if (b < nbx) {
+        constexpr int kSeg = 64 * ColmaxLane<TX>::kCols;
+        const int64_t seg = b % segs_x, split = b / segs_x;
+        const int64_t r0 = split * rpb_x;
+        colmax_block<TX>(x, K, seg, r0, min(T, r0 + rpb_x), red);
+        uint32_t* out = partial + split * K;
+        for (int c = threadIdx.x; c < kSeg; c += kColmaxThreads)
+            if (seg * kSeg + c < K) out[seg * kSeg + c] = red[0][c];
+    } else {
+        b -= nbx;
+        constexpr int kSeg = 64 * ColmaxLane<TW>::kCols;
+        const int64_t seg = b % segs_w, split = b / segs_w;
+        const int64_t r0 = split * rpb_w;
+        colmax_block<TW>(w, K, seg, r0, min(N, r0 + rpb_w), red);
+        uint32_t* out = partial + (splits_x + split) * K;
+        for (int c = threadIdx.x; c < kSeg; c += kColmaxThreads)
+            if (seg * kSeg + c < K) out[seg * kSeg + c] = red[0][c];
     }
 }
 
@@ -136,9 +196,10 @@ hipError_t launch_colmax(const T* x, int64_t rows, int64_t K, uint32_t* out_bits
     if (rows <= 0) return hipSuccess;
     constexpr int kSeg = 64 * ColmaxLane<T>::kCols;
     const int64_t bx = (K + kSeg - 1) / kSeg;
-    // about 4 blocks of 8 waves per CU over 256 CUs, at least 64 rows a block
-    const int64_t want = (1024 + bx - 1) / bx;
-    const int64_t max_split = (rows + 63) / 64;
+    // one resident block of 16 waves per CU over 256 CUs, at least 128 rows a
+    // block (each wave keeps two batches of eight 16-byte loads in flight)
+    const int64_t want = (256 + bx - 1) / bx;
+    const int64_t max_split = (rows + 127) / 128;
     const int64_t by = std::max<int64_t>(1, std::min(want, max_split));
     const int64_t rpb = (rows + by - 1) / by;
     const int64_t by2 = (rows + rpb - 1) / rpb;
@@ -149,10 +210,14 @@ hipError_t launch_colmax(const T* x, int64_t rows, int64_t K, uint32_t* out_bits
 
 // ---- smoothing factor, fold, static scale ------------------------------------
 
-constexpr int kFactorThreads = 256;
+constexpr int kFactorThreads = 64;  // many small blocks: the pass is latency-bound
 
+// With `partial` set, first reduce the per-block column maxima of X_cal (rows
+// [0, splits_x)) and W (rows [splits_x, splits_x + splits_w)) into a_j and w_j
+// (floored) and store them; otherwise a_j and w_j are already in a and w.
 __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
-    const float* __restrict__ a, const float* __restrict__ w, int64_t K, float alpha,
+    float* __restrict__ a, float* __restrict__ w, int64_t K, float alpha,
+    const uint32_t* __restrict__ partial, int splits_x, int splits_w,
     const float* __restrict__ gamma, const float* __restrict__ beta, float* __restrict__ s,
     float* __restrict__ gamma_s, float* __restrict__ beta_s, uint32_t* __restrict__ static_bits) {
     __shared__ float red[kFactorThreads / 64];
@@ -161,10 +226,34 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
     float local = 0.0f;
     for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < K;
          j += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const float aj = a[j];
+        float aj, wj;
+        if (partial) {
+            // eight independent loads in flight per batch
+            auto reduce = [&](int first, int count) {
+                uint32_t m = kFloorBits;
+                for (int i = 0; i < count; i += 8) {
+                    uint32_t v[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        v[u] = (i + u < count) ? partial[(first + i + u) * K + j] : 0u;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) m = max(m, v[u]);
+                }
+                return m;
+            };
+            const uint32_t ab = reduce(0, splits_x);
+            const uint32_t wb = reduce(splits_x, splits_w);
+            aj = __uint_as_float(ab);
+            wj = __uint_as_float(wb);
+            a[j] = aj;
+            w[j] = wj;
+        } else {
+            aj = a[j];
+            wj = w[j];
+        }
         // eq. (4) in fp64, rounded once to fp32
         const float sj = static_cast<float>(pow(static_cast<double>(aj), al) /
-                                            pow(static_cast<double>(w[j]), be));
+                                            pow(static_cast<double>(wj), be));
         s[j] = sj;
         if (gamma) {
             gamma_s[j] = gamma[j] / sj;
@@ -187,47 +276,75 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
 
 // ---- weight smoothing + per-output-channel quantization ------------------------
 
-// One row per team; the team is the whole block (kWqThreads lanes), the row
-// stays in registers (CPT chunks of 8 per lane) between the max and the
-// quantize passes.
-template <typename T, int CPT>
-__global__ __launch_bounds__(1024) void weight_quant_kernel(
+
+// One output row per block; lane t owns chunks t + i*blockDim (i < CPT).  With
+// D > 0 the lane's slice of s is loaded once and kept in registers for every
+// row the block walks, and the loads of the block's next D rows are in flight
+// while the current row is reduced and quantized (a ring of D+1 rows).  The
+// row stays in registers between the absmax and the quantize passes.
+template <typename T, int CPT, int D, int MAXT = 1024>
+__global__ __launch_bounds__(MAXT) void weight_quant_kernel(
     const T* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,
     int8_t* __restrict__ wq, float* __restrict__ w_scale) {
     __shared__ float red[16];
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
+    const int nw = nthr >> 6;
     const int64_t chunks = K / kChunk;
-    for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+    const int64_t G = gridDim.x;
+    constexpr bool CACHE = D > 0;
+
+    RawChunk<T> ring[D + 1][CPT];
+    auto fetch = [&](int64_t n, RawChunk<T> (&r)[CPT]) {
         const T* row = w + n * K;
-        RawChunk<T> raw[CPT];
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int64_t c = tid + static_cast<int64_t>(i) * nthr;
-            if (c < chunks) raw[i] = load_raw(row, c);
+            if (c < chunks) r[i] = load_raw(row, c);
         }
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        if (blockIdx.x + j * G < N) fetch(blockIdx.x + j * G, ring[j]);
+    float sv[CACHE ? CPT : 1][kChunk];
+    if (CACHE) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+            if (c < chunks) load_chunk(s, c, sv[CACHE ? i : 0]);
+        }
+    }
+    for (int64_t n = blockIdx.x; n < N; n += G) {
+        if (n + D * G < N) fetch(n + D * G, ring[D]);
         float v[CPT][kChunk];
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int64_t c = tid + static_cast<int64_t>(i) * nthr;
             if (c < chunks) {
-                float sv[kChunk];
-                load_chunk(s, c, sv);
-                unpack(raw[i], v[i]);
+                float sl[kChunk];
+                if (CACHE) {
+#pragma unroll
+                    for (int e = 0; e < kChunk; ++e) sl[e] = sv[CACHE ? i : 0][e];
+                } else {
+                    load_chunk(s, c, sl);
+                }
+                unpack(ring[0][i], v[i]);
 #pragma unroll
                 for (int e = 0; e < kChunk; ++e) {
-                    v[i][e] = v[i][e] * sv[e];
+                    v[i][e] = v[i][e] * sl[e];
                     m = fmaxf(m, fabsf(v[i][e]));
                 }
             }
         }
         m = wave_max(m);
-        if ((tid & 63) == 0) red[tid >> 6] = m;
-        __syncthreads();
-        m = red[0];
-        for (int i = 1; i < (nthr >> 6); ++i) m = fmaxf(m, red[i]);
-        __syncthreads();  // red is reused by the next row
+        if (nw > 1) {
+            if ((tid & 63) == 0) red[tid >> 6] = m;
+            __syncthreads();
+            m = red[0];
+            for (int i = 1; i < nw; ++i) m = fmaxf(m, red[i]);
+            __syncthreads();  // red is reused by the next row
+        }
         const float d = step_from_absmax(m);
         const float rd = 1.0f / d;
         if (tid == 0) w_scale[n] = d;
@@ -242,6 +359,10 @@ __global__ __launch_bounds__(1024) void weight_quant_kernel(
                 *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
             }
         }
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) ring[j][i] = ring[j + 1][i];
     }
 }
 
@@ -283,32 +404,70 @@ __global__ __launch_bounds__(256) void weight_quant_stream_kernel(
     }
 }
 
-int round_up64(int64_t v) { return static_cast<int>(((v + 63) / 64) * 64); }
-
 template <typename T>
 hipError_t launch_weight_quant(const T* w, int64_t N, int64_t K, const float* s, int8_t* wq,
                                float* w_scale, hipStream_t stream) {
     if (N <= 0) return hipSuccess;
     const int64_t chunks = K / kChunk;
-    int cpt = 1;
-    while (cpt <= 8 && (chunks + cpt - 1) / cpt > 1024) cpt *= 2;
-    if (cpt > 8) {
+    // Measured on the MI355X: one prefetched row (D = 1) beats deeper rings, and
+    // bf16 rows stream best with four 16-byte loads per lane (fp32 rows with
+    // two, which keeps the prefetch ring within the register budget).  Rows
+    // beyond 4096 chunks use eight loads per lane without prefetch (up to 768
+    // lanes), longer ones the two-sweep kernel.
+    if (chunks > 8 * 768) {
         const int64_t grid = std::min<int64_t>(N, 2048);
         weight_quant_stream_kernel<T><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
             w, N, K, s, wq, w_scale);
         return hipGetLastError();
     }
+    constexpr bool kBf16 = sizeof(T) == 2;
+    int cpt, d;
+    if (chunks <= 64) { cpt = 1; d = 1; }
+    else if (chunks <= (kBf16 ? 256 : 2048)) { cpt = 2; d = 1; }
+    else if (chunks <= 4096) { cpt = 4; d = kBf16 ? 1 : 0; }
+    else { cpt = 8; d = 0; }
     const int threads = std::max(64, round_up64((chunks + cpt - 1) / cpt));
-    // enough resident blocks to keep ~16-32 waves per CU busy
-    const int64_t per_cu = std::max(1, 2048 / threads);
-    const int64_t grid = std::min<int64_t>(N, 256 * per_cu);
-    const unsigned g = static_cast<unsigned>(grid);
-    switch (cpt) {
-        case 1: weight_quant_kernel<T, 1><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale); break;
-        case 2: weight_quant_kernel<T, 2><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale); break;
-        case 4: weight_quant_kernel<T, 4><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale); break;
-        default: weight_quant_kernel<T, 8><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale); break;
-    }
+    const int64_t per_cu = std::max(1, 1024 / threads);
+    const unsigned g = static_cast<unsigned>(std::min<int64_t>(N, 256 * per_cu));
+    if (cpt == 1) weight_quant_kernel<T, 1, 1><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
+    else if (cpt == 2) weight_quant_kernel<T, 2, 1><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
+    else if (cpt == 4 && d == 1) weight_quant_kernel<T, kBf16 ? 4 : 2, 1><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
+    else if (cpt == 4) weight_quant_kernel<T, 4, 0><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
+    else weight_quant_kernel<T, 8, 0, 768><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+namespace {
+
+struct Split {
+    int segs = 0;
+    int splits = 0;
+    int64_t rpb = 0;
+};
+
+// Column segments x row splits for one tensor: about one block of 16 waves
+// per CU in total, at least 128 rows per block.
+Split plan_split(int64_t rows, int64_t K, int seg_cols) {
+    Split p;
+    if (rows <= 0) return p;
+    p.segs = static_cast<int>((K + seg_cols - 1) / seg_cols);
+    const int64_t want = (256 + p.segs - 1) / p.segs;
+    const int64_t by = std::max<int64_t>(1, std::min<int64_t>(want, (rows + 127) / 128));
+    p.rpb = (rows + by - 1) / by;
+    p.splits = static_cast<int>((rows + p.rpb - 1) / p.rpb);
+    return p;
+}
+
+template <typename TX, typename TW>
+hipError_t launch_partial(const TX* x, int64_t T, const TW* w, int64_t N, int64_t K,
+                          const Split& px, const Split& pw, uint32_t* partial,
+                          uint32_t* static_bits, hipStream_t stream) {
+    const int64_t blocks = static_cast<int64_t>(px.segs) * px.splits +
+                           static_cast<int64_t>(pw.segs) * pw.splits;
+    colmax_partial_kernel<TX, TW><<<static_cast<unsigned>(blocks), kColmaxThreads, 0, stream>>>(
+        x, T, w, N, K, px.segs, px.rpb, pw.segs, pw.rpb, px.splits, partial, static_bits);
     return hipGetLastError();
 }
 
@@ -322,21 +481,43 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
     uint32_t* xa = reinterpret_cast<uint32_t*>(x_absmax);
     uint32_t* wa = reinterpret_cast<uint32_t*>(w_absmax);
     uint32_t* sb = reinterpret_cast<uint32_t*>(act_scale_static);
-    fill_maxima_kernel<<<static_cast<unsigned>((K + 255) / 256), 256, 0, stream>>>(xa, wa, K, sb);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
 
-    e = (x_dt == Dt::BF16)
-            ? launch_colmax(static_cast<const uint16_t*>(x_cal), T, K, xa, stream)
-            : launch_colmax(static_cast<const float*>(x_cal), T, K, xa, stream);
-    if (e != hipSuccess) return e;
-    e = (w_dt == Dt::BF16) ? launch_colmax(static_cast<const uint16_t*>(w), N, K, wa, stream)
-                           : launch_colmax(static_cast<const float*>(w), N, K, wa, stream);
-    if (e != hipSuccess) return e;
+    // The per-block column maxima need (splits_x + splits_w) * K words of
+    // scratch; the int8 weight output, written only by the last kernel, holds
+    // them when it is large enough.  Otherwise: fill + atomic column maxima.
+    const Split px = plan_split(T, K, x_dt == Dt::BF16 ? 512 : 256);
+    const Split pw = plan_split(N, K, w_dt == Dt::BF16 ? 512 : 256);
+    const int64_t need = static_cast<int64_t>(px.splits + pw.splits) * K * 4;
+    const bool use_partial = N > 0 && need <= N * K;
+    uint32_t* partial = use_partial ? reinterpret_cast<uint32_t*>(wq) : nullptr;
+    if (use_partial) {
+        if (x_dt == Dt::BF16 && w_dt == Dt::BF16)
+            e = launch_partial(static_cast<const uint16_t*>(x_cal), T, static_cast<const uint16_t*>(w), N, K, px, pw, partial, sb, stream);
+        else if (x_dt == Dt::BF16)
+            e = launch_partial(static_cast<const uint16_t*>(x_cal), T, static_cast<const float*>(w), N, K, px, pw, partial, sb, stream);
+        else if (w_dt == Dt::BF16)
+            e = launch_partial(static_cast<const float*>(x_cal), T, static_cast<const uint16_t*>(w), N, K, px, pw, partial, sb, stream);
+        else
+            e = launch_partial(static_cast<const float*>(x_cal), T, static_cast<const float*>(w), N, K, px, pw, partial, sb, stream);
+        if (e != hipSuccess) return e;
+    } else {
+        fill_maxima_kernel<<<static_cast<unsigned>((K + 255) / 256), 256, 0, stream>>>(xa, wa, K, sb);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = (x_dt == Dt::BF16)
+                ? launch_colmax(static_cast<const uint16_t*>(x_cal), T, K, xa, stream)
+                : launch_colmax(static_cast<const float*>(x_cal), T, K, xa, stream);
+        if (e != hipSuccess) return e;
+        e = (w_dt == Dt::BF16) ? launch_colmax(static_cast<const uint16_t*>(w), N, K, wa, stream)
+                               : launch_colmax(static_cast<const float*>(w), N, K, wa, stream);
+        if (e != hipSuccess) return e;
+    }
 
     const int64_t fgrid = std::min<int64_t>((K + kFactorThreads - 1) / kFactorThreads, 1024);
     smooth_factor_kernel<<<static_cast<unsigned>(fgrid), kFactorThreads, 0, stream>>>(
-        x_absmax, w_absmax, K, alpha, gamma, beta, s, gamma_s, beta_s, sb);
+        x_absmax, w_absmax, K, alpha, partial, px.splits, pw.splits, gamma, beta, s, gamma_s,
+        beta_s, sb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 

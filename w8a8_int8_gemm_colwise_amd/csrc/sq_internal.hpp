@@ -11,6 +11,9 @@ namespace sq {
 
 enum class Dt : int { F32 = 0, BF16 = 1 };
 
+// v rounded up to a whole number of 64-lane waves.
+inline int round_up64(int64_t v) { return static_cast<int>(((v + 63) / 64) * 64); }
+
 // Calibration (offline half).
 hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w, Dt w_dt,
                             int64_t N, int64_t K, float alpha, const float* gamma,
