@@ -261,6 +261,84 @@ hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* 
     return hipGetLastError();
 }
 
+
+// Dequantizing epilogue through a per-wave LDS scratch (5 KB: 32 rows of
+// 128 output bytes, 160-byte pitch so the two half-waves' rows land on
+// different banks).  For each 32-row band the wave writes its accumulators in
+// the MFMA layout (2- or 4-byte LDS stores), then reads the band back as
+// 16-byte row chunks and stores whole 128-byte row segments to global memory.
+// Elements are produced exactly as in store_tile.  Chunks that cross the
+// matrix edge, or a Y whose rows are not 16-byte aligned, fall back to
+// element stores.
+template <int OUT, int TM, int TN>
+__device__ __forceinline__ void store_tile_lds(const v16i (&acc)[TM][TN], int row0, int col0,
+                                               int lane, const float* __restrict__ sx,
+                                               int sx_per_token, const float* __restrict__ sw,
+                                               void* __restrict__ Y, int M, int N,
+                                               int8_t* scratch) {
+    constexpr int ES = (OUT == kOutBF16) ? 2 : 4;  // output element bytes
+    constexpr int JW = 128 / (32 * ES);            // 32-column tiles per 128-byte segment
+    constexpr int PITCH = 160;
+    constexpr int EPC = 16 / ES;                   // elements per 16-byte chunk
+    static_assert(TN % JW == 0, "segments cover whole tiles");
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+    const bool vec_ok = ((static_cast<int64_t>(N) * ES) % 16) == 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int jp = 0; jp < TN; jp += JW) {
+#pragma unroll
+            for (int jj = 0; jj < JW; ++jj) {
+                const int j = jp + jj;
+                const int col = col0 + j * 32 + frow;
+                const float dw = (OUT == kOutI32 || col >= N) ? 0.0f : sw[col];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int rin = 8 * g + 4 * fhalf + r;
+                        const int a = acc[i][j][4 * g + r];
+                        int8_t* dst = scratch + rin * PITCH + (jj * 32 + frow) * ES;
+                        if (OUT == kOutI32) {
+                            *reinterpret_cast<int32_t*>(dst) = a;
+                        } else {
+                            const int row = min(row0 + i * 32 + rin, M - 1);
+                            const float dx = sx[sx_per_token ? row : 0];
+                            const float f = dx * dw;
+                            const float y = static_cast<float>(a) * f;
+                            if (OUT == kOutF32)
+                                *reinterpret_cast<float*>(dst) = y;
+                            else
+                                *reinterpret_cast<__bf16*>(dst) = static_cast<__bf16>(y);
+                        }
+                    }
+                }
+            }
+            // 32 rows x 8 chunks of 16 bytes, four per lane; LDS operations of
+            // one wave complete in order, so the reads see the writes above
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int idx = lane + 64 * q;
+                const int rr = idx >> 3, ch = idx & 7;
+                const uint4 v = *reinterpret_cast<const uint4*>(scratch + rr * PITCH + ch * 16);
+                const int grow = row0 + i * 32 + rr;
+                const int gcol = col0 + jp * 32 + ch * EPC;
+                if (grow >= M) continue;
+                int8_t* out = static_cast<int8_t*>(Y) + (static_cast<int64_t>(grow) * N + gcol) * ES;
+                if (vec_ok && gcol + EPC <= N) {
+                    *reinterpret_cast<uint4*>(out) = v;
+                } else {
+                    const int8_t* src = reinterpret_cast<const int8_t*>(&v);
+                    for (int e = 0; e < EPC; ++e)
+                        if (gcol + e < N)
+                            for (int b = 0; b < ES; ++b) out[e * ES + b] = src[e * ES + b];
+                }
+            }
+        }
+    }
+}
+
 // ---- pipelined kernel: direct global->LDS loads, STAGES LDS stages -----------
 //
 // Each stage holds the A rows then the B rows of one BK-byte K slice (rows of
@@ -290,7 +368,8 @@ __device__ __forceinline__ void compiler_fence() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MIN_BLOCKS, int OUT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MIN_BLOCKS, int OUT,
+          bool SCHED = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) void gemm_pipe_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
@@ -351,24 +430,44 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) void gemm_pipe_
 
     const int frow = lane & 31;
     const int fhalf = lane >> 5;
+    // Fragments of K-substep kk+1 are read from LDS while the MFMAs of substep
+    // kk run (two fragment register sets).  With SCHED the machine scheduler
+    // is told to interleave one LDS read after each MFMA.
+    auto load_frags = [&](const int8_t* S, int kk, v4i (&fa)[T::TM], v4i (&fb)[T::TN]) {
+        const int chunk = 2 * kk + fhalf;
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+            fa[i] = *reinterpret_cast<const v4i*>(
+                S + lds_off_k<BK>(wm * T::WM + i * 32 + frow, chunk));
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+            fb[j] = *reinterpret_cast<const v4i*>(
+                S + BM * BK + lds_off_k<BK>(wn * T::WN + j * 32 + frow, chunk));
+    };
     auto compute = [&](const int8_t* S) {
+        constexpr int NKK = BK / 32;
+        v4i fa[2][T::TM], fb[2][T::TN];
+        load_frags(S, 0, fa[0], fb[0]);
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            v4i fa[T::TM], fb[T::TN];
-            const int chunk = 2 * kk + fhalf;
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-                fa[i] = *reinterpret_cast<const v4i*>(
-                    S + lds_off_k<BK>(wm * T::WM + i * 32 + frow, chunk));
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j)
-                fb[j] = *reinterpret_cast<const v4i*>(
-                    S + BM * BK + lds_off_k<BK>(wn * T::WN + j * 32 + frow, chunk));
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < NKK) load_frags(S, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cur][i], fb[cur][j],
+                                                                      acc[i][j], 0, 0, 0);
+            if constexpr (SCHED) {
+                if (kk + 1 < NKK) {
+#pragma unroll
+                    for (int q = 0; q < T::TM + T::TN; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, T::TM * T::TN - (T::TM + T::TN), 0);
+                }
+            }
         }
     };
     // Wait until this wave's transfers into the stage about to be read have
@@ -434,11 +533,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) void gemm_pipe_
         }
     }
 
-    store_tile<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + wn * T::WN, lane, sx, sx_per_token,
-                                  sw, Y, M, N);
+    // epilogue through LDS: every wave has finished reading the stages
+    __syncthreads();
+    constexpr int kScratch = 32 * 160;  // per wave
+    constexpr int kPerStage = kStageBytes / kScratch;
+    static_assert(kPerStage * 2 >= NW, "two stages hold the per-wave scratch");
+    int8_t* scratch = (wave < kPerStage) ? L0 + wave * kScratch : L1 + (wave - kPerStage) * kScratch;
+    store_tile_lds<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + wn * T::WN, lane, sx,
+                                      sx_per_token, sw, Y, M, N, scratch);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MIN_BLOCKS>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MIN_BLOCKS,
+          bool SCHED = false>
 hipError_t run_pipe(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
                     const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -446,15 +552,15 @@ hipError_t run_pipe(const int8_t* xq, const float* sx, bool per_token, const int
     const int pt = per_token ? 1 : 0;
     switch (out) {
         case kOutF32:
-            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutF32>
+            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutF32, SCHED>
                 <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
             break;
         case kOutBF16:
-            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutBF16>
+            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutBF16, SCHED>
                 <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
             break;
         default:
-            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutI32>
+            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutI32, SCHED>
                 <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
             break;
     }
