@@ -567,6 +567,172 @@ hipError_t run_pipe(const int8_t* xq, const float* sx, bool per_token, const int
     return hipGetLastError();
 }
 
+
+// ---- skinny-M kernel (decode: M <= 64): streams W once from HBM ---------------
+//
+// Every W byte is used by at most two 32-row MFMA tiles here, so nothing is
+// staged in LDS: each lane loads its operand fragments straight from global
+// memory.  The assignment of K bytes to MFMA slots is free as long as both
+// operands use the same one, so lane l (row l % 32, half h = l / 32) loads 64
+// contiguous bytes k0 + 64h .. k0 + 64h + 63 of its row for a 128-byte K chunk,
+// and MFMA step s (0..3) consumes bytes 16s..16s+15 of that run.  A block owns
+// NT x 32 output channels; its WPB waves split the K chunks (a contiguous range
+// per wave, or interleaved chunks with the start rotated per block, so that
+// concurrent waves spread over the rows' address range), prefetch the next
+// chunk's W fragments while the current one is multiplied, and sum their int32
+// partial tiles exactly with LDS integer atomics.
+template <int MT, int NT, int WPB, bool ROTATE, int OUT>
+__global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
+    int sx_per_token, const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    constexpr int CW = 32 * NT;  // output channels per block
+    __shared__ int32_t red[MT * 32 * CW];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * CW;
+    const int frow = lane & 31;
+    const int half = lane >> 5;
+
+    for (int i = threadIdx.x; i < MT * 32 * CW; i += 64 * WPB) red[i] = 0;
+
+    const int8_t* brow[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+        brow[u] = B + static_cast<int64_t>(min(n0 + u * 32 + frow, N - 1)) * K + 64 * half;
+    const int8_t* arow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        arow[t] = A + static_cast<int64_t>(min(t * 32 + frow, M - 1)) * K + 64 * half;
+
+    v16i acc[MT][NT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[t][u][r] = 0;
+
+    // chunk i of this wave (0 <= i < cnt) starts at byte 128 * chunk_of(i)
+    const int chunks = K / 128;
+    int first, stride, cnt, rot = 0;
+    if (ROTATE) {
+        first = wave;
+        stride = WPB;
+        cnt = chunks > wave ? (chunks - wave + WPB - 1) / WPB : 0;
+        rot = cnt > 0 ? static_cast<int>((blockIdx.x * 5u) % static_cast<unsigned>(cnt)) : 0;
+    } else {
+        first = static_cast<int>(static_cast<int64_t>(wave) * chunks / WPB);
+        stride = 1;
+        cnt = static_cast<int>(static_cast<int64_t>(wave + 1) * chunks / WPB) - first;
+    }
+    auto chunk_of = [&](int i) {
+        int j = i + rot;
+        j = j >= cnt ? j - cnt : j;
+        return static_cast<int64_t>(first + stride * j) * 128;
+    };
+
+    v4i wn[NT][4];
+    if (cnt > 0) {
+        const int64_t k0 = chunk_of(0);
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) wn[u][s] = *reinterpret_cast<const v4i*>(brow[u] + k0 + 16 * s);
+    }
+    for (int i = 0; i < cnt; ++i) {
+        const int64_t k0 = chunk_of(i);
+        v4i wb[NT][4];
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) wb[u][s] = wn[u][s];
+        if (i + 1 < cnt) {
+            const int64_t k1 = chunk_of(i + 1);
+#pragma unroll
+            for (int u = 0; u < NT; ++u)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) wn[u][s] = *reinterpret_cast<const v4i*>(brow[u] + k1 + 16 * s);
+        }
+        v4i ab[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ab[t][s] = *reinterpret_cast<const v4i*>(arow[t] + k0 + 16 * s);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int u = 0; u < NT; ++u)
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ab[t][s], wb[u][s], acc[t][u], 0, 0, 0);
+    }
+    __syncthreads();  // red is zeroed
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = t * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                atomicAdd(&red[row * CW + u * 32 + frow], acc[t][u][r]);
+            }
+    __syncthreads();
+    for (int i = threadIdx.x; i < MT * 32 * CW; i += 64 * WPB) {
+        const int row = i / CW, col = n0 + i % CW;
+        if (row >= M || col >= N) continue;
+        const int a = red[i];
+        const int64_t o = static_cast<int64_t>(row) * N + col;
+        if (OUT == kOutI32) {
+            static_cast<int32_t*>(Y)[o] = a;
+        } else {
+            const float f = sx[sx_per_token ? row : 0] * sw[col];
+            const float y = static_cast<float>(a) * f;
+            if (OUT == kOutF32)
+                static_cast<float*>(Y)[o] = y;
+            else
+                static_cast<__bf16*>(Y)[o] = static_cast<__bf16>(y);
+        }
+    }
+}
+
+template <int MT, int NT, int WPB, bool ROTATE>
+hipError_t run_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
+                      const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
+    const dim3 grid((N + 32 * NT - 1) / (32 * NT)), block(64 * WPB);
+    const int pt = per_token ? 1 : 0;
+    switch (out) {
+        case kOutF32:
+            gemm_skinny_kernel<MT, NT, WPB, ROTATE, kOutF32>
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            break;
+        case kOutBF16:
+            gemm_skinny_kernel<MT, NT, WPB, ROTATE, kOutBF16>
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            break;
+        default:
+            gemm_skinny_kernel<MT, NT, WPB, ROTATE, kOutI32>
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            break;
+    }
+    return hipGetLastError();
+}
+
+// Configurations measured on the 70B-class FFN shapes (K, N) = (8192, 28672)
+// and (28672, 8192): with many channel blocks, a contiguous K range per wave;
+// with few, more waves per block and rotated interleaved chunks.  Two 32-row
+// tiles (M > 32) re-read X once per 32 channels, so they take 64 channels per
+// block where the grid stays large.
+hipError_t launch_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
+                         const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
+    const int blocks32 = (N + 31) / 32;
+    if (M <= 32) {
+        if (blocks32 >= 512) return run_skinny<1, 1, 8, false>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
+        return run_skinny<1, 1, 16, true>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
+    }
+    if (blocks32 >= 1024) return run_skinny<2, 2, 4, false>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
+    return run_skinny<2, 1, 8, false>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
@@ -574,8 +740,13 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
                        void* y, int out_kind, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    if (M <= 64)
+    if (M <= 64) {
+        // decode shapes: stream W once, K split over the waves of a block
+        if (K % 128 == 0) {
+            return launch_skinny(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
+        }
         return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
+    }
     // pipelined kernels: 128-byte K stages, operand offsets in int32
     const bool pipe_ok = (K % 128 == 0) && M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
     if (pipe_ok) {
