@@ -135,3 +135,16 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(sq, "LIB_PATH", str(tmp_path / "libsq.so"))
     with pytest.raises(RuntimeError):
         sq.lib()
+
+
+def test_library_has_no_unresolved_kernel_stubs():
+    """Every kernel launch in the library resolves to a kernel stub in the same
+    library (a template kernel whose host stub the compiler failed to emit
+    would leave an undefined symbol that only shows at load time)."""
+    import shutil
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", sq.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    assert "__device_stub" not in out

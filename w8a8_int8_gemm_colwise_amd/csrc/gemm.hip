@@ -570,115 +570,111 @@ hipError_t run_pipe(const int8_t* xq, const float* sx, bool per_token, const int
 
 // ---- skinny-M kernel (decode: M <= 64): streams W once from HBM ---------------
 //
-// Every W byte is used by at most two 32-row MFMA tiles here, so nothing is
-// staged in LDS: each lane loads its operand fragments straight from global
-// memory.  The assignment of K bytes to MFMA slots is free as long as both
-// operands use the same one, so lane l (row l % 32, half h = l / 32) loads 64
-// contiguous bytes k0 + 64h .. k0 + 64h + 63 of its row for a 128-byte K chunk,
-// and MFMA step s (0..3) consumes bytes 16s..16s+15 of that run.  A block owns
-// NT x 32 output channels; its WPB waves split the K chunks (a contiguous range
-// per wave, or interleaved chunks with the start rotated per block, so that
-// concurrent waves spread over the rows' address range), prefetch the next
-// chunk's W fragments while the current one is multiplied, and sum their int32
-// partial tiles exactly with LDS integer atomics.
-template <int MT, int NT, int WPB, bool ROTATE, int OUT>
+// Every W byte meets at most two 32-row MFMA tiles here, so the kernel is bound
+// by the weight stream.  A block owns 32 output channels and its WPB waves
+// split the K chunks (128 bytes each) into contiguous ranges.  Each wave runs
+// its own ring of ST LDS stages with no block-level barrier: one stage holds
+// the chunk's 32 W rows and MT x 32 X rows (128 bytes each), filled by
+// global_load_lds transfers that each move eight whole 128-byte row segments,
+// so every load instruction covers full cache lines.  16-byte slot c of row r
+// is stored at slot c ^ ((r >> 1) & 7), which keeps the fragment reads free of
+// bank conflicts.  The K-to-MFMA-slot assignment is free as long as both
+// operands share it: lane l (row l % 32, half h = l / 32) takes bytes
+// 64h + 16s .. 64h + 16s + 15 of the chunk in MFMA step s.  The waves' int32
+// partial tiles are summed exactly with LDS integer atomics.
+template <int MT, int WPB, int ST>
+struct Skinny {
+    static constexpr int kGroups = 1 + MT;                 // 32-row groups per stage
+    static constexpr int kStage = kGroups * 4096;          // bytes per stage
+    static constexpr int kXfers = 4 * kGroups;             // 1 KB transfers per stage
+    static constexpr int kRing = WPB * ST * kStage;        // LDS ring bytes per block
+};
+
+// fill one stage with the 128-byte K chunk `chunk` of every row it holds
+template <int XFERS>
+__device__ __forceinline__ void skinny_issue(const int8_t* const* src, int8_t* stage, int chunk) {
+    const int64_t k0 = static_cast<int64_t>(chunk) * 128;
+#pragma unroll
+    for (int q = 0; q < XFERS; ++q)
+        __builtin_amdgcn_global_load_lds(src[q] + k0, (lds_ptr_t)(stage + q * 1024), 16, 0, 0);
+}
+
+template <int MT, int WPB, int ST, int OUT>
 __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
-    constexpr int CW = 32 * NT;  // output channels per block
-    __shared__ int32_t red[MT * 32 * CW];
+    using S = Skinny<MT, WPB, ST>;
+    static_assert(ST >= 2 && ST <= 3, "2 or 3 stages");
+    __shared__ __attribute__((aligned(1024))) int8_t ring[S::kRing];
+    __shared__ int32_t red[MT * 32 * 32];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * CW;
+    const int n0 = blockIdx.x * 32;
     const int frow = lane & 31;
     const int half = lane >> 5;
 
-    for (int i = threadIdx.x; i < MT * 32 * CW; i += 64 * WPB) red[i] = 0;
+    for (int i = threadIdx.x; i < MT * 32 * 32; i += 64 * WPB) red[i] = 0;
 
-    const int8_t* brow[NT];
+    // transfer q of a stage: group g = q / 4 (0 = W, 1.. = X tiles), rows
+    // 8 (q % 4) .. 8 (q % 4) + 7 of the group; lane -> row + lane / 8 and the
+    // source slot whose swizzled position is lane % 8
+    int8_t* my = ring + wave * ST * S::kStage;
+    const int8_t* src[4 * (1 + MT)];
 #pragma unroll
-    for (int u = 0; u < NT; ++u)
-        brow[u] = B + static_cast<int64_t>(min(n0 + u * 32 + frow, N - 1)) * K + 64 * half;
-    const int8_t* arow[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-        arow[t] = A + static_cast<int64_t>(min(t * 32 + frow, M - 1)) * K + 64 * half;
-
-    v16i acc[MT][NT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int u = 0; u < NT; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[t][u][r] = 0;
-
-    // chunk i of this wave (0 <= i < cnt) starts at byte 128 * chunk_of(i)
+    for (int q = 0; q < S::kXfers; ++q) {
+        const int g = q / 4;
+        const int row = 8 * (q % 4) + (lane >> 3);
+        const int slot = (lane & 7) ^ ((row >> 1) & 7);
+        src[q] = g == 0 ? B + static_cast<int64_t>(min(n0 + row, N - 1)) * K + 16 * slot
+                        : A + static_cast<int64_t>(min((g - 1) * 32 + row, M - 1)) * K + 16 * slot;
+    }
     const int chunks = K / 128;
-    int first, stride, cnt, rot = 0;
-    if (ROTATE) {
-        first = wave;
-        stride = WPB;
-        cnt = chunks > wave ? (chunks - wave + WPB - 1) / WPB : 0;
-        rot = cnt > 0 ? static_cast<int>((blockIdx.x * 5u) % static_cast<unsigned>(cnt)) : 0;
-    } else {
-        first = static_cast<int>(static_cast<int64_t>(wave) * chunks / WPB);
-        stride = 1;
-        cnt = static_cast<int>(static_cast<int64_t>(wave + 1) * chunks / WPB) - first;
-    }
-    auto chunk_of = [&](int i) {
-        int j = i + rot;
-        j = j >= cnt ? j - cnt : j;
-        return static_cast<int64_t>(first + stride * j) * 128;
-    };
+    const int first = static_cast<int>(static_cast<int64_t>(wave) * chunks / WPB);
+    const int cnt = static_cast<int>(static_cast<int64_t>(wave + 1) * chunks / WPB) - first;
+    v16i acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0;
 
-    v4i wn[NT][4];
-    if (cnt > 0) {
-        const int64_t k0 = chunk_of(0);
-#pragma unroll
-        for (int u = 0; u < NT; ++u)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) wn[u][s] = *reinterpret_cast<const v4i*>(brow[u] + k0 + 16 * s);
-    }
+    for (int i = 0; i < ST - 1 && i < cnt; ++i) skinny_issue<S::kXfers>(src, my + (i % ST) * S::kStage, first + i);
     for (int i = 0; i < cnt; ++i) {
-        const int64_t k0 = chunk_of(i);
-        v4i wb[NT][4];
+        compiler_fence();
+        if (i + ST - 1 < cnt)
+            skinny_issue<S::kXfers>(src, my + ((i + ST - 1) % ST) * S::kStage, first + i + ST - 1);
+        // stages issued after stage i may stay in flight
+        const int younger = min(cnt - 1, i + ST - 1) - i;
+        if (younger >= 2) wait_vmcnt<2 * S::kXfers>();
+        else if (younger == 1) wait_vmcnt<S::kXfers>();
+        else wait_vmcnt<0>();
+        compiler_fence();
+        const int8_t* st = my + (i % ST) * S::kStage;
+        v4i wb[4], ab[MT][4];
 #pragma unroll
-        for (int u = 0; u < NT; ++u)
+        for (int s = 0; s < 4; ++s) {
+            const int off = frow * 128 + 16 * ((4 * half + s) ^ ((frow >> 1) & 7));
+            wb[s] = *reinterpret_cast<const v4i*>(st + off);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) wb[u][s] = wn[u][s];
-        if (i + 1 < cnt) {
-            const int64_t k1 = chunk_of(i + 1);
-#pragma unroll
-            for (int u = 0; u < NT; ++u)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) wn[u][s] = *reinterpret_cast<const v4i*>(brow[u] + k1 + 16 * s);
+            for (int t = 0; t < MT; ++t) ab[t][s] = *reinterpret_cast<const v4i*>(st + (1 + t) * 4096 + off);
         }
-        v4i ab[MT][4];
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) ab[t][s] = *reinterpret_cast<const v4i*>(arow[t] + k0 + 16 * s);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int t = 0; t < MT; ++t)
-#pragma unroll
-                for (int u = 0; u < NT; ++u)
-                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ab[t][s], wb[u][s], acc[t][u], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ab[t][s], wb[s], acc[t], 0, 0, 0);
     }
+    compiler_fence();
     __syncthreads();  // red is zeroed
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int u = 0; u < NT; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = t * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                atomicAdd(&red[row * CW + u * 32 + frow], acc[t][u][r]);
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int row = t * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            atomicAdd(&red[row * 32 + frow], acc[t][r]);
+        }
     __syncthreads();
-    for (int i = threadIdx.x; i < MT * 32 * CW; i += 64 * WPB) {
-        const int row = i / CW, col = n0 + i % CW;
+    for (int i = threadIdx.x; i < MT * 32 * 32; i += 64 * WPB) {
+        const int row = i >> 5, col = n0 + (i & 31);
         if (row >= M || col >= N) continue;
         const int a = red[i];
         const int64_t o = static_cast<int64_t>(row) * N + col;
@@ -695,42 +691,36 @@ __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
     }
 }
 
-template <int MT, int NT, int WPB, bool ROTATE>
+template <int MT, int WPB, int ST>
 hipError_t run_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
                       const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
-    const dim3 grid((N + 32 * NT - 1) / (32 * NT)), block(64 * WPB);
+    const dim3 grid((N + 31) / 32), block(64 * WPB);
     const int pt = per_token ? 1 : 0;
     switch (out) {
         case kOutF32:
-            gemm_skinny_kernel<MT, NT, WPB, ROTATE, kOutF32>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            gemm_skinny_kernel<MT, WPB, ST, kOutF32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
             break;
         case kOutBF16:
-            gemm_skinny_kernel<MT, NT, WPB, ROTATE, kOutBF16>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            gemm_skinny_kernel<MT, WPB, ST, kOutBF16><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
             break;
         default:
-            gemm_skinny_kernel<MT, NT, WPB, ROTATE, kOutI32>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            gemm_skinny_kernel<MT, WPB, ST, kOutI32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
             break;
     }
     return hipGetLastError();
 }
 
-// Configurations measured on the 70B-class FFN shapes (K, N) = (8192, 28672)
-// and (28672, 8192): with many channel blocks, a contiguous K range per wave;
-// with few, more waves per block and rotated interleaved chunks.  Two 32-row
-// tiles (M > 32) re-read X once per 32 channels, so they take 64 channels per
-// block where the grid stays large.
+// Configurations measured on cold 70B-class FFN weights, (K, N) = (8192, 28672)
+// and (28672, 8192): four waves per block when there are many channel blocks,
+// eight when there are few; two 32-row X tiles take three stages.
 hipError_t launch_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
                          const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
-    const int blocks32 = (N + 31) / 32;
+    const int blocks = (N + 31) / 32;
     if (M <= 32) {
-        if (blocks32 >= 512) return run_skinny<1, 1, 8, false>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
-        return run_skinny<1, 1, 16, true>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
+        if (blocks >= 512) return run_skinny<1, 4, 2>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
+        return run_skinny<1, 8, 2>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
     }
-    if (blocks32 >= 1024) return run_skinny<2, 2, 4, false>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
-    return run_skinny<2, 1, 8, false>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
+    return run_skinny<2, 4, 3>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
 }
 
 }  // namespace
