@@ -262,101 +262,98 @@ hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* 
 }
 
 
-// Dequantizing epilogue through a per-wave LDS scratch (5 KB: 32 rows of
-// 128 output bytes, 160-byte pitch so the two half-waves' rows land on
-// different banks).  For each 32-row band the wave writes its accumulators in
-// the MFMA layout (2- or 4-byte LDS stores), then reads the band back as
-// 16-byte row chunks and stores whole 128-byte row segments to global memory.
-// Elements are produced exactly as in store_tile.  Chunks that cross the
-// matrix edge, or a Y whose rows are not 16-byte aligned, fall back to
-// element stores.
+// Epilogue for accumulators computed as W x X^T (MFMA operands swapped): in a
+// 32x32 tile lane l holds output row l % 32 and, in registers 4g..4g+3, the
+// four consecutive output columns 8g + 4(l / 32) .. +3.  Per 32-row slice of
+// the wave tile, the dequantized values go to a per-wave LDS scratch of padded
+// rows (8-byte writes for bf16, 16-byte writes for f32 / int32; the padding
+// keeps a write instruction free of bank conflicts) and leave as whole
+// 16-byte chunks, several lanes per row, so each global store instruction
+// covers complete 128-byte row segments.  sxs / sws: LDS copies of the scales
+// of the wave tile's rows and columns.  The dequantization is the library's
+// fixed order: f = s_x * s_w, then y = float(acc) * f, rounded once to the
+// output type.
 template <int OUT, int TM, int TN>
-__device__ __forceinline__ void store_tile_lds(const v16i (&acc)[TM][TN], int row0, int col0,
-                                               int lane, const float* __restrict__ sx,
-                                               int sx_per_token, const float* __restrict__ sw,
-                                               void* __restrict__ Y, int M, int N,
-                                               int8_t* scratch) {
+__device__ __forceinline__ void store_tile_t(const v16i (&acc)[TM][TN], int row0, int col0,
+                                             int lane, const float* sxs, const float* sws,
+                                             void* __restrict__ Y, int M, int N,
+                                             int8_t* scratch) {
     constexpr int ES = (OUT == kOutBF16) ? 2 : 4;  // output element bytes
-    constexpr int JW = 128 / (32 * ES);            // 32-column tiles per 128-byte segment
-    constexpr int PITCH = 160;
-    constexpr int EPC = 16 / ES;                   // elements per 16-byte chunk
-    static_assert(TN % JW == 0, "segments cover whole tiles");
-    const int frow = lane & 31;
-    const int fhalf = lane >> 5;
+    constexpr int SEG = TN * 32 * ES;              // bytes of one row of the wave tile
+    constexpr int PITCH = SEG + (ES == 2 ? 8 : 16);
+    constexpr int CPR = SEG / 16;                  // 16-byte chunks per row
+    constexpr int EPC = 16 / ES;                   // elements per chunk
+    static_assert((32 * CPR) % 64 == 0, "whole chunks per lane");
+    const int fr = lane & 31;
+    const int h = lane >> 5;
     const bool vec_ok = ((static_cast<int64_t>(N) * ES) % 16) == 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+        const float dx = (OUT == kOutI32) ? 0.0f : sxs[i * 32 + fr];
 #pragma unroll
-        for (int jp = 0; jp < TN; jp += JW) {
+        for (int j = 0; j < TN; ++j) {
 #pragma unroll
-            for (int jj = 0; jj < JW; ++jj) {
-                const int j = jp + jj;
-                const int col = col0 + j * 32 + frow;
-                const float dw = (OUT == kOutI32 || col >= N) ? 0.0f : sw[col];
+            for (int g = 0; g < 4; ++g) {
+                const int c = j * 32 + 8 * g + 4 * h;  // first of the lane's 4 columns
+                int8_t* dst = scratch + fr * PITCH + c * ES;
+                if (OUT == kOutI32) {
+                    v4i v;
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+                    *reinterpret_cast<v4i*>(dst) = v;
+                } else {
+                    const float4 w = *reinterpret_cast<const float4*>(sws + c);
+                    const float dw[4] = {w.x, w.y, w.z, w.w};
+                    float y[4];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int rin = 8 * g + 4 * fhalf + r;
-                        const int a = acc[i][j][4 * g + r];
-                        int8_t* dst = scratch + rin * PITCH + (jj * 32 + frow) * ES;
-                        if (OUT == kOutI32) {
-                            *reinterpret_cast<int32_t*>(dst) = a;
-                        } else {
-                            const int row = min(row0 + i * 32 + rin, M - 1);
-                            const float dx = sx[sx_per_token ? row : 0];
-                            const float f = dx * dw;
-                            const float y = static_cast<float>(a) * f;
-                            if (OUT == kOutF32)
-                                *reinterpret_cast<float*>(dst) = y;
-                            else
-                                *reinterpret_cast<__bf16*>(dst) = static_cast<__bf16>(y);
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        const float f = dx * dw[e];
+                        y[e] = static_cast<float>(acc[i][j][4 * g + e]) * f;
+                    }
+                    if (OUT == kOutF32) {
+                        *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+                    } else {
+                        typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+                        bf4 b;
+                        for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>(y[e]);
+                        *reinterpret_cast<bf4*>(dst) = b;
                     }
                 }
             }
-            // 32 rows x 8 chunks of 16 bytes, four per lane; LDS operations of
-            // one wave complete in order, so the reads see the writes above
+        }
+        // LDS operations of one wave complete in order: the reads see the writes
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int idx = lane + 64 * q;
-                const int rr = idx >> 3, ch = idx & 7;
-                const uint4 v = *reinterpret_cast<const uint4*>(scratch + rr * PITCH + ch * 16);
-                const int grow = row0 + i * 32 + rr;
-                const int gcol = col0 + jp * 32 + ch * EPC;
-                if (grow >= M) continue;
-                int8_t* out = static_cast<int8_t*>(Y) + (static_cast<int64_t>(grow) * N + gcol) * ES;
-                if (vec_ok && gcol + EPC <= N) {
-                    *reinterpret_cast<uint4*>(out) = v;
-                } else {
-                    const int8_t* src = reinterpret_cast<const int8_t*>(&v);
-                    for (int e = 0; e < EPC; ++e)
-                        if (gcol + e < N)
-                            for (int b = 0; b < ES; ++b) out[e * ES + b] = src[e * ES + b];
-                }
+        for (int q = 0; q < 32 * CPR / 64; ++q) {
+            const int idx = lane + 64 * q;
+            const int rr = idx / CPR, ch = idx % CPR;
+            const uint4 v = *reinterpret_cast<const uint4*>(scratch + rr * PITCH + ch * 16);
+            const int grow = row0 + i * 32 + rr;
+            const int gcol = col0 + ch * EPC;
+            if (grow >= M) continue;
+            int8_t* out = static_cast<int8_t*>(Y) + (static_cast<int64_t>(grow) * N + gcol) * ES;
+            if (vec_ok && gcol + EPC <= N) {
+                *reinterpret_cast<uint4*>(out) = v;
+            } else {
+                const int8_t* src = reinterpret_cast<const int8_t*>(&v);
+                for (int e = 0; e < EPC; ++e)
+                    if (gcol + e < N)
+                        for (int b = 0; b < ES; ++b) out[e * ES + b] = src[e * ES + b];
             }
         }
     }
 }
 
-// ---- pipelined kernel: direct global->LDS loads, STAGES LDS stages -----------
-//
-// Each stage holds the A rows then the B rows of one BK-byte K slice (rows of
-// BK bytes, 16-byte chunks permuted by swz_k).  A stage is filled with
-// global_load_lds_dwordx4: one instruction moves 64 lanes x 16 bytes into 1 KB
-// of consecutive LDS, so lane q of a transfer fetches the global chunk whose
-// swizzled LDS slot is q.  No VGPRs hold tiles in flight, so STAGES-1 stages
-// are in flight while the matrix cores work on another.  The stages are
-// distinct LDS arrays so the compiler can see that reading one stage does not
-// depend on the transfers into the others; the waits are explicit vmcnt
-// counts followed by a plain s_barrier, fenced for both the IR optimizers and
-// the machine scheduler.
+// ---- pipeline helpers ---------------------------------------------------------
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    // vmcnt and expcnt at their maxima (no wait), lgkmcnt 0
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
 // Ordering point for both the IR optimizers (memory clobber) and the machine
@@ -368,26 +365,63 @@ __device__ __forceinline__ void compiler_fence() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MIN_BLOCKS, int OUT,
-          bool SCHED = false>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) void gemm_pipe_kernel(
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));
+}
+
+// global_load_lds_dwordx4 in its scalar-base form: lane l copies the 16 bytes
+// at base + voff(l) to LDS address lds + 16 l; base and lds are wave-uniform.
+// Issued from inline asm, the transfer is invisible to the compiler's wait
+// counter tracking, so the kernel's own vmcnt waits are the only ones: the
+// compiler otherwise drains every transfer in flight at each loop back-edge.
+// The compiler uses M0 for nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const int8_t* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// ---- ping-pong pipelined kernel ---------------------------------------------
+//
+// Eight waves, two per SIMD, in two groups of four (one wave of each group on
+// every SIMD).  Each wave alternates a memory phase -- issue its share of the
+// global->LDS transfers for stage t+STAGES-1, read all MFMA fragments of
+// stage t from LDS into registers -- and a compute phase of back-to-back
+// MFMAs on those registers.  Group 1 starts one phase late, so on every SIMD
+// one wave's MFMAs run while the other wave's memory phase is in flight, and
+// each block-wide barrier closes a compute phase of one group and a memory
+// phase of the other.  Ordering (barrier n closes phase n of group 0 and
+// phase n-1 of group 1):
+//  * a stage buffer is refilled only in the memory phase after the one in
+//    which both groups finished reading it (each wave drains its LDS reads
+//    before arriving at a barrier);
+//  * every wave waits for its own transfers of stage t+1 before the barrier
+//    that precedes either group's memory phase of stage t+1.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OUT>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
-    constexpr int NW = WAVES_M * WAVES_N;
+    static_assert(WAVES_M * WAVES_N == 8, "two groups of four waves");
     constexpr int kRows = BM + BN;
     constexpr int kStageBytes = kRows * BK;
-    constexpr int kCPR = BK / 16;              // 16-byte chunks per row
-    constexpr int kRowsPerXfer = 1024 / BK;    // 1 KB per wave-wide transfer
-    constexpr int kIssues = kRows / kRowsPerXfer;
-    constexpr int IPW = kIssues / NW;
-    static_assert(IPW * NW == kIssues, "stage divides over the waves");
+    constexpr int kCPR = BK / 16;            // 16-byte chunks per row
+    constexpr int kRowsPerXfer = 1024 / BK;  // 1 KB per wave-wide transfer
+    constexpr int IPW = kRows / kRowsPerXfer / 8;
+    constexpr int NKK = BK / 32;
+    static_assert(IPW * 8 * kRowsPerXfer == kRows, "stage divides over the waves");
     static_assert(BM % kRowsPerXfer == 0, "a transfer never straddles A and B");
-    static_assert(STAGES >= 3 && STAGES <= 4, "3 or 4 stages");
-    __shared__ __attribute__((aligned(1024))) int8_t L0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) int8_t L1[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) int8_t L2[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) int8_t L3[STAGES > 3 ? kStageBytes : 16];
+    static_assert(STAGES >= 3, "a refill needs two phases of slack");
+    constexpr int kEpiPitch = T::TN * 32 * (OUT == kOutBF16 ? 2 : 4) + (OUT == kOutBF16 ? 8 : 16);
+    static_assert(8 * 32 * kEpiPitch <= STAGES * kStageBytes, "epilogue scratch fits");
+    static_assert(BM + BN <= 512, "one scale per thread");
+    __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * kStageBytes];
+    __shared__ __attribute__((aligned(16))) float scales[BM + BN];  // row scales, then column scales
 
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
@@ -396,28 +430,41 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) void gemm_pipe_
     const int m0 = tmi * BM, n0 = tni * BN;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int group = wave >> 2;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    // byte offset (from A or B) of the source chunk of every transfer this
-    // lane takes part in; the caller guarantees M*K and N*K fit in int32
     int src_off[IPW];
     bool src_a[IPW];
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-        const int q = (wave * IPW + i) * 64 + lane;  // 16-byte slot within the stage
+        const int x = wave * IPW + i;
+        const int q = x * 64 + lane;
         const int row = q / kCPR;
         const int c = (q % kCPR) ^ swz_k<BK>(row);
-        src_a[i] = row < BM;  // uniform per transfer: BM is a multiple of 16
+        src_a[i] = x * kRowsPerXfer < BM;
         src_off[i] = src_a[i] ? min(m0 + row, M - 1) * K + c * 16
                               : min(n0 + row - BM, N - 1) * K + c * 16;
     }
-    auto issue = [&](int8_t* stage, int k0) {
+    const int KT = K / BK;
+    auto issue = [&](int t) {
+        int8_t* stage = lds + (t % STAGES) * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int8_t* g = (src_a[i] ? A : B) + (src_off[i] + k0);
-            __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(stage + (wave * IPW + i) * 1024), 16, 0, 0);
-        }
+        for (int i = 0; i < IPW; ++i)
+            dma16(src_a[i] ? A : B, static_cast<uint32_t>(src_off[i] + t * BK),
+                  lds_addr(stage + (wave * IPW + i) * 1024));
+    };
+    // wait for this wave's transfers of stage t; later stages may stay in flight
+    auto wait_stage = [&](int t) {
+        const int younger = min(KT - 1, t + STAGES - 2) - t;
+        if (younger >= 2) wait_vmcnt<2 * IPW>();
+        else if (younger == 1) wait_vmcnt<IPW>();
+        else wait_vmcnt<0>();
+    };
+    auto bar = [&]() {
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
     };
 
     v16i acc[T::TM][T::TN];
@@ -430,137 +477,78 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) void gemm_pipe_
 
     const int frow = lane & 31;
     const int fhalf = lane >> 5;
-    // Fragments of K-substep kk+1 are read from LDS while the MFMAs of substep
-    // kk run (two fragment register sets).  With SCHED the machine scheduler
-    // is told to interleave one LDS read after each MFMA.
-    auto load_frags = [&](const int8_t* S, int kk, v4i (&fa)[T::TM], v4i (&fb)[T::TN]) {
-        const int chunk = 2 * kk + fhalf;
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i)
-            fa[i] = *reinterpret_cast<const v4i*>(
-                S + lds_off_k<BK>(wm * T::WM + i * 32 + frow, chunk));
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j)
-            fb[j] = *reinterpret_cast<const v4i*>(
-                S + BM * BK + lds_off_k<BK>(wn * T::WN + j * 32 + frow, chunk));
-    };
-    auto compute = [&](const int8_t* S) {
-        constexpr int NKK = BK / 32;
-        v4i fa[2][T::TM], fb[2][T::TN];
-        load_frags(S, 0, fa[0], fb[0]);
+    v4i fa[NKK][T::TM], fb[NKK][T::TN];
+
+    // the tile's scales: loaded before the first transfers are issued, stored
+    // to LDS after stage 0 has landed (the store waits for every load in
+    // flight, stages 1.. included, once per tile)
+    float scale = 0.0f;
+    const int st = threadIdx.x;
+    if (OUT != kOutI32 && st < BM + BN)
+        scale = st < BM ? sx[sx_per_token ? min(m0 + st, M - 1) : 0] : sw[min(n0 + st - BM, N - 1)];
+    compiler_fence();
+    for (int t = 0; t < STAGES - 1 && t < KT; ++t) issue(t);
+    wait_stage(0);
+    if (OUT != kOutI32 && st < BM + BN) scales[st] = scale;
+    bar();
+    if (group == 1) bar();
+    for (int t = 0; t < KT; ++t) {
+        // memory phase
+        if (t + STAGES - 1 < KT) issue(t + STAGES - 1);
+        const int8_t* S = lds + (t % STAGES) * kStageBytes;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            const int cur = kk & 1;
-            if (kk + 1 < NKK) load_frags(S, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+                fa[kk][i] = *reinterpret_cast<const v4i*>(
+                    S + lds_off_k<BK>(wm * T::WM + i * 32 + frow, 2 * kk + fhalf));
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+                fb[kk][j] = *reinterpret_cast<const v4i*>(
+                    S + BM * BK + lds_off_k<BK>(wn * T::WN + j * 32 + frow, 2 * kk + fhalf));
+        }
+        compiler_fence();
+        wait_lgkmcnt0();
+        if (group == 1 && t + 1 < KT) wait_stage(t + 1);
+        bar();
+        // compute phase
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cur][i], fb[cur][j],
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[kk][j], fa[kk][i],
                                                                       acc[i][j], 0, 0, 0);
-            if constexpr (SCHED) {
-                if (kk + 1 < NKK) {
-#pragma unroll
-                    for (int q = 0; q < T::TM + T::TN; ++q) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, T::TM * T::TN - (T::TM + T::TN), 0);
-                }
-            }
-        }
-    };
-    // Wait until this wave's transfers into the stage about to be read have
-    // landed (`younger` later stages may stay in flight), then meet the other
-    // waves: after the barrier every wave's part of the stage is in LDS and
-    // every wave has finished reading the stage that the next issue reuses.
-    auto sync_stage = [&](int younger) {
-        if (younger >= 2) wait_vmcnt<2 * IPW>();
-        else if (younger == 1) wait_vmcnt<IPW>();
-        else wait_vmcnt<0>();
         compiler_fence();
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
-    };
-    // One pipeline step for stage t held in `cur`; the step then refills
-    // `nxt` (the buffer read one step earlier) with stage t + STAGES - 1.  In
-    // the steady state STAGES-2 younger stages are in flight and the refill is
-    // unconditional, so the step is straight-line code.  The buffers are passed
-    // as the LDS arrays themselves so the compiler keeps their identities.
-    const int KT = K / BK;
-    auto steady = [&](int t, const int8_t* cur, int8_t* nxt) {
-        wait_vmcnt<(STAGES - 2) * IPW>();
-        compiler_fence();
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
-        issue(nxt, (t + STAGES - 1) * BK);
-        compute(cur);
-    };
-    auto drain = [&](int t, const int8_t* cur, int8_t* nxt) {
-        sync_stage(min(KT - 1 - t, STAGES - 2));
-        if (t + STAGES - 1 < KT) issue(nxt, (t + STAGES - 1) * BK);
-        compute(cur);
-    };
-
-    issue(L0, 0);
-    if (KT > 1) issue(L1, BK);
-    if (STAGES > 3 && KT > 2) issue(L2, 2 * BK);
-    // steady state in groups of STAGES steps (buffers rotate 0..STAGES-1)
-    int t = 0;
-    if constexpr (STAGES == 4) {
-        for (; t + 2 * STAGES - 1 <= KT; t += STAGES) {
-            steady(t, L0, L3);
-            steady(t + 1, L1, L0);
-            steady(t + 2, L2, L1);
-            steady(t + 3, L3, L2);
-        }
-        for (int g = 0; g < 2; ++g, t += STAGES) {
-            if (t < KT) drain(t, L0, L3);
-            if (t + 1 < KT) drain(t + 1, L1, L0);
-            if (t + 2 < KT) drain(t + 2, L2, L1);
-            if (t + 3 < KT) drain(t + 3, L3, L2);
-        }
-    } else {
-        for (; t + 2 * STAGES - 1 <= KT; t += STAGES) {
-            steady(t, L0, L2);
-            steady(t + 1, L1, L0);
-            steady(t + 2, L2, L1);
-        }
-        for (int g = 0; g < 2; ++g, t += STAGES) {
-            if (t < KT) drain(t, L0, L2);
-            if (t + 1 < KT) drain(t + 1, L1, L0);
-            if (t + 2 < KT) drain(t + 2, L2, L1);
-        }
+        if (group == 0 && t + 1 < KT) wait_stage(t + 1);
+        bar();
     }
+    if (group == 0) bar();
 
-    // epilogue through LDS: every wave has finished reading the stages
     __syncthreads();
-    constexpr int kScratch = 32 * 160;  // per wave
-    constexpr int kPerStage = kStageBytes / kScratch;
-    static_assert(kPerStage * 2 >= NW, "two stages hold the per-wave scratch");
-    int8_t* scratch = (wave < kPerStage) ? L0 + wave * kScratch : L1 + (wave - kPerStage) * kScratch;
-    store_tile_lds<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + wn * T::WN, lane, sx,
-                                      sx_per_token, sw, Y, M, N, scratch);
+    store_tile_t<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + wn * T::WN, lane,
+                                    scales + wm * T::WM, scales + BM + wn * T::WN, Y, M, N,
+                                    lds + wave * (32 * kEpiPitch));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int MIN_BLOCKS,
-          bool SCHED = false>
-hipError_t run_pipe(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
-                    const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
+hipError_t run_pp(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
+                  const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const dim3 grid(tiles), block(64 * WAVES_M * WAVES_N);
+    const dim3 grid(tiles), block(512);
     const int pt = per_token ? 1 : 0;
     switch (out) {
         case kOutF32:
-            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutF32, SCHED>
+            gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutF32>
                 <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
             break;
         case kOutBF16:
-            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutBF16, SCHED>
+            gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutBF16>
                 <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
             break;
         default:
-            gemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, MIN_BLOCKS, kOutI32, SCHED>
+            gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutI32>
                 <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
             break;
     }
@@ -590,13 +578,16 @@ struct Skinny {
     static constexpr int kRing = WPB * ST * kStage;        // LDS ring bytes per block
 };
 
-// fill one stage with the 128-byte K chunk `chunk` of every row it holds
+// fill one stage with the 128-byte K chunk `chunk` of every row it holds:
+// transfers 0..3 read W (B), the others X (A); off[q] is the lane's byte
+// offset of its row segment at K = 0
 template <int XFERS>
-__device__ __forceinline__ void skinny_issue(const int8_t* const* src, int8_t* stage, int chunk) {
-    const int64_t k0 = static_cast<int64_t>(chunk) * 128;
+__device__ __forceinline__ void skinny_issue(const int8_t* A, const int8_t* B, const uint32_t* off,
+                                             int8_t* stage, int chunk) {
+    const uint32_t k0 = static_cast<uint32_t>(chunk) * 128u;
 #pragma unroll
     for (int q = 0; q < XFERS; ++q)
-        __builtin_amdgcn_global_load_lds(src[q] + k0, (lds_ptr_t)(stage + q * 1024), 16, 0, 0);
+        dma16(q < 4 ? B : A, off[q] + k0, lds_addr(stage + q * 1024));
 }
 
 template <int MT, int WPB, int ST, int OUT>
@@ -608,7 +599,7 @@ __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
     __shared__ __attribute__((aligned(1024))) int8_t ring[S::kRing];
     __shared__ int32_t red[MT * 32 * 32];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * 32;
     const int frow = lane & 31;
     const int half = lane >> 5;
@@ -619,14 +610,14 @@ __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
     // 8 (q % 4) .. 8 (q % 4) + 7 of the group; lane -> row + lane / 8 and the
     // source slot whose swizzled position is lane % 8
     int8_t* my = ring + wave * ST * S::kStage;
-    const int8_t* src[4 * (1 + MT)];
+    uint32_t off[4 * (1 + MT)];  // the caller guarantees N*K and M*K < 2^31
 #pragma unroll
     for (int q = 0; q < S::kXfers; ++q) {
         const int g = q / 4;
         const int row = 8 * (q % 4) + (lane >> 3);
         const int slot = (lane & 7) ^ ((row >> 1) & 7);
-        src[q] = g == 0 ? B + static_cast<int64_t>(min(n0 + row, N - 1)) * K + 16 * slot
-                        : A + static_cast<int64_t>(min((g - 1) * 32 + row, M - 1)) * K + 16 * slot;
+        off[q] = static_cast<uint32_t>(g == 0 ? min(n0 + row, N - 1) * K + 16 * slot
+                                              : min((g - 1) * 32 + row, M - 1) * K + 16 * slot);
     }
     const int chunks = K / 128;
     const int first = static_cast<int>(static_cast<int64_t>(wave) * chunks / WPB);
@@ -637,11 +628,12 @@ __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0;
 
-    for (int i = 0; i < ST - 1 && i < cnt; ++i) skinny_issue<S::kXfers>(src, my + (i % ST) * S::kStage, first + i);
+    for (int i = 0; i < ST - 1 && i < cnt; ++i)
+        skinny_issue<S::kXfers>(A, B, off, my + (i % ST) * S::kStage, first + i);
     for (int i = 0; i < cnt; ++i) {
         compiler_fence();
         if (i + ST - 1 < cnt)
-            skinny_issue<S::kXfers>(src, my + ((i + ST - 1) % ST) * S::kStage, first + i + ST - 1);
+            skinny_issue<S::kXfers>(A, B, off, my + ((i + ST - 1) % ST) * S::kStage, first + i + ST - 1);
         // stages issued after stage i may stay in flight
         const int younger = min(cnt - 1, i + ST - 1) - i;
         if (younger >= 2) wait_vmcnt<2 * S::kXfers>();
@@ -732,25 +724,26 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     if (M <= 64) {
         // decode shapes: stream W once, K split over the waves of a block
-        if (K % 128 == 0) {
+        if (K % 128 == 0 && N * K < (int64_t(1) << 31)) {
             return launch_skinny(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
         }
         return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
     }
-    // pipelined kernels: 128-byte K stages, operand offsets in int32
-    const bool pipe_ok = (K % 128 == 0) && M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
-    if (pipe_ok) {
-        // pick the tile by whole waves of 256 CUs: a 256x256 tile does twice the
-        // work of a 256x128 tile at slightly higher efficiency
+    // ping-pong kernels: K a multiple of the 128-byte stage of the 256x128
+    // tile, operand offsets in int32
+    const bool pp_ok = (K % 128 == 0) && M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
+    if (pp_ok) {
+        // pick the tile by whole rounds of 256 CUs: a 256x256 tile does twice
+        // the work of a 256x128 tile at slightly higher efficiency
         const int64_t t_big = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t t_mid = ((M + 255) / 256) * ((N + 127) / 128);
         const int64_t cost_big = ((t_big + 255) / 256) * 2 * 100;
         const int64_t cost_mid = ((t_mid + 255) / 256) * 105;
         if (cost_big <= cost_mid)
-            return run_pipe<256, 256, 2, 4, 64, 4, 1>(xq, x_scale, x_per_token, wq, w_scale, m, n, k,
-                                                      y, out_kind, stream);
-        return run_pipe<256, 128, 4, 2, 128, 3, 1>(xq, x_scale, x_per_token, wq, w_scale, m, n, k,
-                                                   y, out_kind, stream);
+            return run_pp<256, 256, 2, 4, 64, 3>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y,
+                                                 out_kind, stream);
+        return run_pp<256, 128, 4, 2, 128, 3>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y,
+                                              out_kind, stream);
     }
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 127) / 128);
     if (big_tiles >= 256)
