@@ -103,6 +103,11 @@ def main():
     ap.add_argument("--decode-m", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the attainable-ceiling probes (MFMA loop, HBM read and copy)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run one 256 MiB copy_kernel before the warmup (the known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -169,6 +174,15 @@ def main():
             if ev is not None:
                 ev[i][3].record(stream)
 
+    if args.traffic_probe:
+        from w8a8_int8_gemm_colwise_amd import probes
+        nb = 256 << 20
+        a = torch.ones(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        probes.copy(dev, a, b, nb)
+        torch.cuda.synchronize()
+        del a, b
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -220,25 +234,46 @@ def main():
         }
     value = tot_ops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel by time: the GEMM (MFMA-bound) unless the HBM-bound
-    # calls take longer
+    # attainable ceilings on this machine (after the timed region)
+    attain = None
+    if not args.no_probes:
+        from w8a8_int8_gemm_colwise_amd import probes
+        attain = {"mfma_i8_TOPS": round(probes.mfma_i8_tops(dev), 1),
+                  "hbm_read_GBs": round(probes.hbm_read_gbs(dev), 1),
+                  "hbm_copy_GBs": round(probes.hbm_copy_gbs(dev), 1),
+                  "how": "libsqprobe: int8 MFMA loop on operands rne(N(0,40^2)) clipped to "
+                         "+-127; streaming read of 1 GiB; copy of 512 MiB (read + written bytes)"}
+
+    # dominant kernel by time: the GEMM unless the HBM-bound calls take longer
     tg, tc, ta = t_gemm.sum(), t_cal.sum(), t_act.sum()
     launches = n
-    if tg >= max(tc, ta):
+    skinny = all(L["M"] <= 64 for L in layers)
+    gemm_bytes = sum(_alg(L["spec"], L["M"])[3] for L in layers)
+    if tg >= max(tc, ta) and not skinny:
         ach = gemm_ops / tg / 1e12
-        traffic = _traffic(launches)
-        roof = {"kernel": "sq_gemm_w8a8 (gemm_kernel)", "bound": "mfma", "achieved": round(ach, 1),
-                "peak": PEAK_INT8_TOPS, "unit": "TOPS", "frac": round(ach / PEAK_INT8_TOPS, 4),
-                "traffic": traffic, "launches_per_step": launches,
-                "avg_launch_us": round(tg / launches * 1e6, 2),
+        roof = {"kernel": "sq_gemm_w8a8 (gemm_pp_kernel)", "bound": "mfma",
+                "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": _traffic(launches),
+                "launches_per_step": launches, "avg_launch_us": round(tg / launches * 1e6, 2),
                 "alg_ops_per_launch": gemm_ops / launches}
+        if attain:
+            roof["attainable"] = attain["mfma_i8_TOPS"]
+            roof["frac_attainable"] = round(ach / attain["mfma_i8_TOPS"], 4)
     else:
-        name, t, b = ("sq_calibrate", tc, cal_b) if tc >= ta else ("sq_smooth_quantize_act", ta, act_b)
+        if tg >= max(tc, ta):
+            name, t, b = "sq_gemm_w8a8 (gemm_skinny_kernel)", tg, gemm_bytes
+        elif tc >= ta:
+            name, t, b = "sq_calibrate", tc, cal_b
+        else:
+            name, t, b = "sq_smooth_quantize_act", ta, act_b
         ach = b / t / 1e9
         roof = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
                 "launches_per_step": launches, "avg_launch_us": round(t / launches * 1e6, 2),
                 "alg_bytes_per_launch": b / launches}
+        if attain:
+            roof["attainable"] = attain["hbm_copy_GBs"]
+            roof["frac_attainable"] = round(ach / attain["hbm_copy_GBs"], 4)
 
     out = {
         "metric": "W8A8 GEMM INT8 TOPS (% MFMA peak) + fused quantize GB/s (% HBM peak)",
@@ -266,6 +301,8 @@ def main():
                       "frac": round(cal_b / tc / 1e9 / PEAK_HBM_GBS, 4)},
         "per_linear": per,
     }
+    if attain:
+        out["attainable"] = attain
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
     print(json.dumps(out), flush=True)

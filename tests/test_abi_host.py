@@ -148,3 +148,22 @@ def test_library_has_no_unresolved_kernel_stubs():
     out = subprocess.run([nm, "-D", "--undefined-only", sq.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     assert "__device_stub" not in out
+
+
+def test_probe_library_exports_and_validates():
+    """libsqprobe.so (the benchmark's attainable-ceiling probes) exports what
+    include/sq_probe.h declares and rejects invalid arguments before launching."""
+    from w8a8_int8_gemm_colwise_amd import probes
+    text = open(os.path.join(ROOT, "include", "sq_probe.h")).read()
+    names = set(re.findall(r"^\s*int\s+(sqp_\w+)\s*\(", text, flags=re.M))
+    assert names == {"sqp_mfma_i8", "sqp_read", "sqp_copy"}
+    out = subprocess.run(["nm", "-D", "--defined-only", probes.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert names <= set(re.findall(r" T (sqp_\w+)$", out, flags=re.M))
+    L = probes.lib()
+    assert L.sqp_mfma_i8(None, 4, 8, P, None) == 1
+    assert L.sqp_mfma_i8(P, 4, 12, P, None) == 1          # iters not a multiple of 8
+    assert L.sqp_read(P, 100, 4, P, None) == 1            # bytes not a multiple of 16
+    assert L.sqp_read(MIS, 64, 4, P, None) == 1           # misaligned
+    assert L.sqp_copy(P, MIS, 64, 4, None) == 1
+    assert L.sqp_copy(P, P + 64, 0, 4, None) == 1

@@ -1,4 +1,5 @@
-"""Build libsq.so (the HIP kernels + C ABI) for gfx950 with hipcc.
+"""Build libsq.so (the HIP kernels + C ABI) and libsqprobe.so (the
+benchmark's attainable-ceiling probes) for gfx950 with hipcc.
 
     python -m w8a8_int8_gemm_colwise_amd.build
 
@@ -20,6 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "sq")
 LIB = os.path.join(HERE, "libsq.so")
 SOURCES = ["abi.hip", "calibrate.hip", "act_quant.hip", "gemm.hip"]
+PROBE_LIB = os.path.join(HERE, "libsqprobe.so")
+PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -47,18 +50,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {PROBE_LIB}")
     return LIB
 
 
