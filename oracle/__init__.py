@@ -67,7 +67,11 @@ def lib():
         L.orc_quant_static.restype = ctypes.c_int64
         L.orc_gemm_i32.argtypes = [i8p, i8p, i64, i64, i64, vp]
         L.orc_gemm_i32.restype = ci
-        L.orc_dequant.argtypes = [vp, f32p, ci, f32p, i64, i64, f32p]
+        L.orc_dequant.argtypes = [vp, f32p, ci, f32p, ci, i64, i64, f32p]
+        L.orc_weight_quant_per_tensor.argtypes = [vp, ci, i64, i64, f32p, i8p]
+        L.orc_weight_quant_per_tensor.restype = ctypes.c_float
+        L.orc_quant_dynamic_per_tensor.argtypes = [f32p, i64, i64, i8p]
+        L.orc_quant_dynamic_per_tensor.restype = ctypes.c_float
         L.orc_f32_to_bf16.argtypes = [f32p, i64, vp]
         L.orc_ln_f64.argtypes = [vp, ci, i64, i64, vp, vp, ctypes.c_double, vp]
         L.orc_num_threads.restype = ci
@@ -144,6 +148,16 @@ def weight_quant(w: np.ndarray, s, rows=None):
     return wq, sc
 
 
+def weight_quant_per_tensor(w: np.ndarray, s):
+    """Per-tensor weight step ([Review] §6.3, SmoothQuant-O1..O3): (codes, [dw])."""
+    N, K = w.shape
+    p, dt = _raw(w)
+    s = _f32(s)
+    wq = np.empty((N, K), np.int8)
+    d = lib().orc_weight_quant_per_tensor(p, dt, N, K, s.ctypes.data, wq.ctypes.data)
+    return wq, np.array([d], np.float32)
+
+
 def weight_quant_per_input(w: np.ndarray, s):
     N, K = w.shape
     p, dt = _raw(w)
@@ -203,6 +217,15 @@ def quant_per_token(xhat):
     return q, sc
 
 
+def quant_dynamic_per_tensor(xhat):
+    """Dynamic per-tensor activation step ([Review] §6.3, SmoothQuant-O2): (codes, [d])."""
+    xhat = _f32(xhat)
+    M, K = xhat.shape
+    q = np.empty((M, K), np.int8)
+    d = lib().orc_quant_dynamic_per_tensor(xhat.ctypes.data, M, K, q.ctypes.data)
+    return q, np.array([d], np.float32)
+
+
 def quant_static(xhat, scale):
     xhat = _f32(xhat)
     M, K = xhat.shape
@@ -225,13 +248,14 @@ def gemm_i32(xq, wq) -> np.ndarray:
     return acc
 
 
-def dequant(acc, x_scale, w_scale, per_token: bool = True) -> np.ndarray:
+def dequant(acc, x_scale, w_scale, per_token: bool = True,
+            w_per_tensor: bool = False) -> np.ndarray:
     acc = np.ascontiguousarray(acc, dtype=np.int32)
     xs, ws = _f32(x_scale), _f32(w_scale)
     M, N = acc.shape
     y = np.empty((M, N), np.float32)
     lib().orc_dequant(acc.ctypes.data, xs.ctypes.data, int(bool(per_token)), ws.ctypes.data,
-                      M, N, y.ctypes.data)
+                      int(bool(w_per_tensor)), M, N, y.ctypes.data)
     return y
 
 
@@ -277,25 +301,38 @@ def ref_smoothed_linear_f64(x, w, s) -> np.ndarray:
 
 # ---- whole-path composition (oracle side) ------------------------------------
 
-def calibrate(x_cal, w, alpha, gamma=None, beta=None, rows=None):
-    """Offline half: colmax of X_cal and W, eq. (4), smoothed per-output-channel
-    int8 weights, optional LayerNorm fold and the static activation scale."""
+def calibrate(x_cal, w, alpha, gamma=None, beta=None, rows=None, w_per_tensor=False):
+    """Offline half: colmax of X_cal and W, eq. (4), smoothed int8 weights
+    (per output channel, or per tensor for the [Review] §6.3 O1-O3 settings),
+    optional LayerNorm fold and the static activation scale."""
     a = colmax(x_cal)
     wm = colmax(w)
     s = smooth_factor(a, wm, alpha)
-    wq, w_scale = weight_quant(w, s, rows=rows)
+    if w_per_tensor:
+        if rows is not None:
+            raise ValueError("a per-tensor weight step needs every row")
+        wq, w_scale = weight_quant_per_tensor(w, s)
+    else:
+        wq, w_scale = weight_quant(w, s, rows=rows)
     out = dict(a=a, wmax=wm, s=s, wq=wq, w_scale=w_scale, static_scale=static_scale(a, s))
     if gamma is not None:
         out["g_s"], out["b_s"] = ln_fold(gamma, beta, s)
     return out
 
 
-def smooth_quantize_act(x, s=None, g_s=None, b_s=None, eps=1e-5, static=None, rows=None):
-    """Runtime half on the activation side; returns (codes, scales, n_saturated)."""
+def smooth_quantize_act(x, s=None, g_s=None, b_s=None, eps=1e-5, static=None, rows=None,
+                        dynamic_per_tensor=False):
+    """Runtime half on the activation side; returns (codes, scales, n_saturated).
+    dynamic_per_tensor: one step over the whole batch ([Review] §6.3 O2)."""
     if s is not None:
         xhat = act_smooth(x, s, rows=rows)
     else:
         xhat = act_ln(x, g_s, b_s, eps=eps, rows=rows)
+    if dynamic_per_tensor:
+        if rows is not None:
+            raise ValueError("a per-tensor step needs every token")
+        q, d = quant_dynamic_per_tensor(xhat)
+        return q, d, 0
     if static is None:
         q, sc = quant_per_token(xhat)
         return q, sc, 0
@@ -303,11 +340,11 @@ def smooth_quantize_act(x, s=None, g_s=None, b_s=None, eps=1e-5, static=None, ro
     return q, np.array([static], np.float32), sat
 
 
-def gemm_w8a8(xq, x_scale, wq, w_scale, per_token=True, out="f32"):
+def gemm_w8a8(xq, x_scale, wq, w_scale, per_token=True, out="f32", w_per_tensor=False):
     acc = gemm_i32(xq, wq)
     if out == "i32":
         return acc
-    y = dequant(acc, x_scale, w_scale, per_token=per_token)
+    y = dequant(acc, x_scale, w_scale, per_token=per_token, w_per_tensor=w_per_tensor)
     if out == "bf16":
         return f32_to_bf16(y)
     return y

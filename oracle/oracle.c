@@ -140,6 +140,28 @@ void orc_weight_quant(const void* w, int dt, int64_t N, int64_t K, const float* 
     }
 }
 
+/* [Review] §6.3: the SmoothQuant-O1/O2/O3 settings quantize the weight per
+ * TENSOR -- one step for the whole smoothed weight:
+ * dw = RN(max(FLOOR, max_{n,k} |What|) / 127), wq = clamp(rne(RN(What / dw))).
+ * Two plain passes over W (the maximum, then the codes).  Returns dw. */
+float orc_weight_quant_per_tensor(const void* w, int dt, int64_t N, int64_t K, const float* s,
+                                  int8_t* wq) {
+    float m = 0.0f;
+#pragma omp parallel for schedule(static) reduction(max : m)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(load_elem(w, dt, n * K + k) * s[k]);
+            if (v > m) m = v;
+        }
+    }
+    const float d = step_from_absmax(m);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            wq[n * K + k] = quantize_code((load_elem(w, dt, n * K + k) * s[k]) / d);
+    return d;
+}
+
 void orc_weight_quant_per_input(const void* w, int dt, int64_t N, int64_t K, const float* s,
                                 int8_t* wq, float* col_scale) {
     for (int64_t k = 0; k < K; ++k) {
@@ -260,6 +282,23 @@ void orc_quant_per_token(const float* xhat, int64_t M, int64_t K, int8_t* q, flo
     }
 }
 
+/* [Review] §6.3: SmoothQuant-O2 (and the naive W8A8 baseline of the same
+ * section) quantizes the activation with one DYNAMIC per-tensor step, taken
+ * over every token of the batch: d = RN(max(FLOOR, max_{t,k} |xhat|) / 127),
+ * q = clamp(rne(RN(xhat / d))).  Returns d. */
+float orc_quant_dynamic_per_tensor(const float* xhat, int64_t M, int64_t K, int8_t* q) {
+    float mx = 0.0f;
+#pragma omp parallel for schedule(static) reduction(max : mx)
+    for (int64_t i = 0; i < M * K; ++i) {
+        float v = fabsf(xhat[i]);
+        if (v > mx) mx = v;
+    }
+    const float d = step_from_absmax(mx);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M * K; ++i) q[i] = quantize_code(xhat[i] / d);
+    return d;
+}
+
 /* [Review] §2.5 (static) with one per-tensor scale; codes beyond the range
  * saturate at +-127 ([Edge] §三 clips to int8). */
 int64_t orc_quant_static(const float* xhat, int64_t M, int64_t K, float scale, int8_t* q) {
@@ -298,12 +337,12 @@ int orc_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64
 /* [Edge] §三: the output is (float)acc times the product of the activation
  * scale and the weight scale of output channel n, in that order. */
 void orc_dequant(const int32_t* acc, const float* x_scale, int x_per_token,
-                 const float* w_scale, int64_t M, int64_t N, float* y) {
+                 const float* w_scale, int w_per_tensor, int64_t M, int64_t N, float* y) {
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         float dx = x_per_token ? x_scale[m] : x_scale[0];
         for (int64_t n = 0; n < N; ++n) {
-            float f = dx * w_scale[n];
+            float f = dx * (w_per_tensor ? w_scale[0] : w_scale[n]);
             y[m * N + n] = (float)acc[m * N + n] * f;
         }
     }

@@ -85,6 +85,15 @@ float orc_canonical_sum(const float* v, int64_t K);
 /* Per-token dynamic int8: d_t = RN(max(FLOOR, max_k|xhat|)/127). */
 void orc_quant_per_token(const float* xhat, int64_t M, int64_t K, int8_t* q, float* scale);
 
+/* Per-tensor weight step (SmoothQuant-O1..O3): one dw for the whole smoothed
+ * weight; returns dw and writes the codes [N, K]. */
+float orc_weight_quant_per_tensor(const void* w, int dt, int64_t N, int64_t K, const float* s,
+                                  int8_t* wq);
+
+/* Dynamic per-tensor activation step (SmoothQuant-O2): one step for every
+ * token of the batch; returns it and writes the codes [M, K]. */
+float orc_quant_dynamic_per_tensor(const float* xhat, int64_t M, int64_t K, int8_t* q);
+
 /* Static per-tensor int8 with a given scale; returns the number of codes
  * that saturated (|RN(xhat/d)| rounded beyond 127). */
 int64_t orc_quant_static(const float* xhat, int64_t M, int64_t K, float scale, int8_t* q);
@@ -94,9 +103,10 @@ int64_t orc_quant_static(const float* xhat, int64_t M, int64_t K, float scale, i
 int orc_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
                  int32_t* acc);
 
-/* Dequant: y = RN((float)acc * RN(dx_t * dw_n)); x_per_token=0 reads dx[0]. */
+/* Dequant: y = RN((float)acc * RN(dx_t * dw_n)); x_per_token=0 reads dx[0],
+ * w_per_tensor=1 reads dw[0]. */
 void orc_dequant(const int32_t* acc, const float* x_scale, int x_per_token,
-                 const float* w_scale, int64_t M, int64_t N, float* y);
+                 const float* w_scale, int w_per_tensor, int64_t M, int64_t N, float* y);
 
 /* fp32 -> bf16 bit pattern, round to nearest even. */
 void orc_f32_to_bf16(const float* y, int64_t n, uint16_t* out);

@@ -406,3 +406,87 @@ def test_smoothing_reduces_error_on_outlier_layer():
     e_sq = run(cal["s"])
     e_naive = run(np.ones(spec.K, np.float32))
     assert e_sq < 0.5 * e_naive
+
+
+# ---- per-tensor settings SmoothQuant-O1/O2/O3 ([Review] §6.3) ----------------------
+
+def _golden_kv(name):
+    kv = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.split()
+    return kv
+
+
+def _bits(x):
+    return int(np.array(np.float32(x)).view(np.uint32))
+
+
+def test_per_tensor_hand_example():
+    """tests/golden/per_tensor_example.txt: the weight step, the dynamic
+    activation step and every code, worked by hand (one exact tie included)."""
+    g = _golden_kv("per_tensor_example.txt")
+    w = np.array(g["w"], np.float32).reshape([int(v) for v in g["w_shape"]])
+    wq, dw = oracle.weight_quant_per_tensor(w, np.ones(w.shape[1], np.float32))
+    assert _bits(dw[0]) == int(g["w_step_bits"][0], 16)
+    assert wq.ravel().tolist() == [int(v) for v in g["w_codes"]]
+    _, row_steps = oracle.weight_quant(w, np.ones(w.shape[1], np.float32))
+    assert [_bits(v) for v in row_steps] == [int(v, 16) for v in g["w_row_step_bits"]]
+    x = np.array(g["x"], np.float32).reshape([int(v) for v in g["x_shape"]])
+    xq, dx = oracle.quant_dynamic_per_tensor(x)
+    assert _bits(dx[0]) == int(g["x_step_bits"][0], 16)
+    assert xq.ravel().tolist() == [int(v) for v in g["x_codes"]]
+    _, tok_steps = oracle.quant_per_token(x)
+    assert [_bits(v) for v in tok_steps] == [int(v, 16) for v in g["x_row_step_bits"]]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_per_tensor_step_is_max_of_finer_steps(seed):
+    """step = RN(max(FLOOR, m)/127) is monotone in m, so the per-tensor weight
+    step equals the largest per-output-channel step and the dynamic per-tensor
+    activation step the largest per-token step, bit for bit; rows that attain
+    the maximum get identical codes under both granularities, and every other
+    row uses at most as many levels."""
+    rng = np.random.default_rng(seed)
+    N, K = 37, 96
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[5, 7] = 0.9
+    s = rng.uniform(0.2, 5.0, K).astype(np.float32)
+    wq_t, dw = oracle.weight_quant_per_tensor(w, s)
+    wq_c, dwn = oracle.weight_quant(w, s)
+    assert dw[0] == dwn.max()
+    top = np.flatnonzero(dwn == dw[0])
+    assert np.array_equal(wq_t[top], wq_c[top])
+    assert np.all(np.abs(wq_t).max(axis=1) <= np.abs(wq_c).max(axis=1))
+    xh = (rng.standard_normal((29, K)) * 3).astype(np.float32)
+    xh[11, 3] = -60.0
+    q_t, d = oracle.quant_dynamic_per_tensor(xh)
+    q_c, dt = oracle.quant_per_token(xh)
+    assert d[0] == dt.max()
+    top = np.flatnonzero(dt == d[0])
+    assert np.array_equal(q_t[top], q_c[top])
+
+
+def test_dynamic_per_tensor_error_bound():
+    """The symmetric quantizer's bound |x - q d| <= d/2 holds for every element
+    (a dynamic step never clamps), and the batch maximum maps to +-127."""
+    rng = np.random.default_rng(3)
+    xh = (rng.standard_normal((64, 128)) * 2).astype(np.float32)
+    q, d = oracle.quant_dynamic_per_tensor(xh)
+    err = np.abs(xh.astype(np.float64) - q.astype(np.float64) * np.float64(d[0]))
+    assert err.max() <= np.float64(d[0]) / 2 * (1 + 2.0 ** -20)
+    assert int(np.abs(q).max()) == 127
+
+
+def test_dequant_per_tensor_weight_is_broadcast():
+    """A per-tensor weight step dequantizes exactly like a per-channel vector
+    filled with that step."""
+    rng = np.random.default_rng(4)
+    acc = rng.integers(-2 ** 30, 2 ** 30, size=(7, 13), dtype=np.int64).astype(np.int32)
+    xs = rng.uniform(1e-3, 1e-1, 7).astype(np.float32)
+    d = np.float32(0.0123)
+    y_t = oracle.dequant(acc, xs, np.array([d], np.float32), per_token=True, w_per_tensor=True)
+    y_c = oracle.dequant(acc, xs, np.full(13, d, np.float32), per_token=True)
+    assert np.array_equal(y_t.view(np.uint32), y_c.view(np.uint32))
