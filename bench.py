@@ -67,7 +67,8 @@ def _traffic(gemm_launches: int):
         return None
 
 
-def cpu_baseline(workload, max_tokens: int = 256):
+def cpu_baseline(workload, max_tokens: int = 256, w_mode: str = "per_channel",
+                 a_mode: str = "per_token"):
     """Time the CPU oracle on a bounded sample of the workload: every linear's
     full calibration and weight quantization, then activation quantization,
     int8 GEMM and dequant for the first ``max_tokens`` tokens."""
@@ -76,13 +77,21 @@ def cpu_baseline(workload, max_tokens: int = 256):
 
     ops = 0.0
     t_total = 0.0
+    wpt = w_mode == "per_tensor"
     for spec in workload.layers:
         xc, w = datagen.calibration_x(spec), datagen.weights(spec)
         x = datagen.eval_x(spec)[:max_tokens]
+        g = b = None
+        if spec.ln:
+            g, b = datagen.ln_params(spec)
         t0 = time.perf_counter()
-        cal = oracle.calibrate(xc, w, spec.alpha)
-        xq, xs, _ = oracle.smooth_quantize_act(x, s=cal["s"])
-        y = oracle.gemm_w8a8(xq, xs, cal["wq"], cal["w_scale"], out="bf16")
+        cal = oracle.calibrate(xc, w, spec.alpha, g, b, w_per_tensor=wpt)
+        kw = dict(g_s=cal["g_s"], b_s=cal["b_s"]) if spec.ln else dict(s=cal["s"])
+        xq, xs, _ = oracle.smooth_quantize_act(
+            x, static=cal["static_scale"] if a_mode == "static" else None,
+            dynamic_per_tensor=a_mode == "dynamic_per_tensor", **kw)
+        y = oracle.gemm_w8a8(xq, xs, cal["wq"], cal["w_scale"], per_token=a_mode == "per_token",
+                             out="bf16", w_per_tensor=wpt)
         t_total += time.perf_counter() - t0
         ops += 2.0 * x.shape[0] * spec.N * spec.K
         del y
@@ -101,6 +110,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="opt6.7b", choices=sorted(WORKLOADS))
     ap.add_argument("--decode-m", type=int, default=64)
+    ap.add_argument("--setting", default="colwise", choices=["colwise", "O1", "O2", "O3"],
+                    help="weight / activation step granularity: colwise = per output channel + "
+                         "per token (default); O1-O3 = the per-tensor weight settings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-probes", action="store_true",
@@ -119,6 +131,7 @@ def main():
     import datagen
     import w8a8_int8_gemm_colwise_amd as sq
 
+    w_mode, a_mode = sq.SETTINGS[args.setting]
     cid = WORKLOADS[args.workload]
     wl = datagen.workload(cid, M=args.decode_m) if cid == 3 else datagen.workload(cid)
     dev = torch.device("cuda:0")
@@ -144,7 +157,9 @@ def main():
             L["cal_out"]["ln_gamma_s"] = torch.empty(K, **f32)
             L["cal_out"]["ln_beta_s"] = torch.empty(K, **f32)
         L["xq"] = torch.empty((M, K), dtype=torch.int8, device=dev)
-        L["xs"] = torch.empty(M, **f32)
+        L["xs"] = torch.empty(M if a_mode == "per_token" else 1, **f32)
+        if w_mode == "per_tensor":
+            L["cal_out"]["w_scale"] = torch.empty(1, **f32)
         L["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         L["M"] = M
         layers.append(L)
@@ -158,19 +173,22 @@ def main():
             if ev is not None:
                 ev[i][0].record(stream)
             cal = sq.sq_calibrate(L["xc"], L["w"], spec.alpha, L.get("g"), L.get("b"),
-                                  out=L["cal_out"])
+                                  out=L["cal_out"], w_mode=w_mode)
             if ev is not None:
                 ev[i][1].record(stream)
+            st = cal["static_scale"] if a_mode == "static" else None
+            xs = None if a_mode == "static" else L["xs"]
             if spec.ln:
-                sq.sq_smooth_quantize_act(L["x"], None, cal["ln_gamma_s"], cal["ln_beta_s"], 1e-5,
-                                          "per_token", xq=L["xq"], x_scale=L["xs"])
+                _, xs_used = sq.sq_smooth_quantize_act(L["x"], None, cal["ln_gamma_s"],
+                                                       cal["ln_beta_s"], 1e-5, a_mode, st,
+                                                       xq=L["xq"], x_scale=xs)
             else:
-                sq.sq_smooth_quantize_act(L["x"], cal["s"], mode="per_token", xq=L["xq"],
-                                          x_scale=L["xs"])
+                _, xs_used = sq.sq_smooth_quantize_act(L["x"], cal["s"], mode=a_mode,
+                                                       static_scale=st, xq=L["xq"], x_scale=xs)
             if ev is not None:
                 ev[i][2].record(stream)
-            sq.sq_gemm_w8a8(L["xq"], L["xs"], cal["wq"], cal["w_scale"], "per_token", "bf16",
-                            y=L["y"])
+            sq.sq_gemm_w8a8(L["xq"], xs_used, cal["wq"], cal["w_scale"], a_mode, "bf16",
+                            y=L["y"], w_mode=w_mode)
             if ev is not None:
                 ev[i][3].record(stream)
 
@@ -290,7 +308,8 @@ def main():
         "data": "synthetic (seeded; outlier channels at +-U(50,120); bf16 inputs)",
         "config": {"workload": wl.name, "M": layers[0]["M"],
                    "linears_KN": [[L["spec"].K, L["spec"].N] for L in layers],
-                   "alpha": wl.layers[0].alpha, "act_scale": "per_token", "y_dtype": "bf16",
+                   "alpha": wl.layers[0].alpha, "setting": args.setting, "w_scale": w_mode,
+                   "act_scale": a_mode, "y_dtype": "bf16",
                    "step": "sq_calibrate + sq_smooth_quantize_act + sq_gemm_w8a8 per linear"},
         "roofline": roof,
         "gemm": {"TOPS": round(gemm_ops / tg / 1e12, 1),
@@ -304,7 +323,7 @@ def main():
     if attain:
         out["attainable"] = attain
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens, w_mode, a_mode)
     print(json.dumps(out), flush=True)
 
 

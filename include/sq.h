@@ -46,6 +46,8 @@
  *                added to partial floor(k/8) mod 256 in increasing k from +0,
  *                then p[i] = RN(p[i] + p[i+d]) for d = 128, 64, ..., 1.
  *   per-token:   dx_t = RN(max(FLOOR, max_k |xh_k|) / 127);  static: dx_t = dx_static
+ *   dynamic per-tensor: dx_t = dx = RN(max(FLOOR, max_{t,k} |xh|) / 127) over the batch
+ *   per-tensor weight:  dw_n = dw = RN(max(FLOOR, max_{n,k} |What|) / 127)
  *   xq   = clamp(rne(RN(xh_k / dx_t)))
  *   acc  = sum_k xq[t,k] * wq[n,k]   (exact int32)
  *   y    = RN(RN_f32(acc) * RN(dx_t * dw_n));  bf16 output = y rounded to
@@ -62,7 +64,7 @@ extern "C" {
 
 typedef struct ihipStream_t* sq_stream_t; /* a hipStream_t */
 
-#define SQ_ABI_VERSION 1
+#define SQ_ABI_VERSION 2
 #define SQ_MAX_K 133120          /* largest multiple of 64 with 127*127*K < 2^31 */
 #define SQ_ABSMAX_FLOOR 1e-7f    /* floor of every absolute maximum */
 
@@ -79,7 +81,21 @@ typedef enum {
 
 typedef enum { SQ_F32 = 0, SQ_BF16 = 1, SQ_I8 = 2, SQ_I32 = 3 } sq_dtype;
 
-typedef enum { SQ_PER_TOKEN = 0, SQ_STATIC_PER_TENSOR = 1 } sq_act_mode;
+/* Activation step granularity ([Review] §2.5-§2.6 dynamic / static, per token
+ * / per tensor; §6.3 uses all three). */
+typedef enum {
+    SQ_PER_TOKEN = 0,          /* dynamic, one step per token */
+    SQ_STATIC_PER_TENSOR = 1,  /* one step from calibration (dx_static) */
+    SQ_DYNAMIC_PER_TENSOR = 2  /* dynamic, one step for the whole batch */
+} sq_act_mode;
+
+/* Weight step granularity.  SQ_W_PER_CHANNEL: one step per output channel
+ * (the column-wise scale of Y = XW).  SQ_W_PER_TENSOR: one step for the whole
+ * weight, as in the SmoothQuant-O1/O2/O3 settings of [Review] §6.3:
+ *   O1 = SQ_W_PER_TENSOR + SQ_PER_TOKEN
+ *   O2 = SQ_W_PER_TENSOR + SQ_DYNAMIC_PER_TENSOR
+ *   O3 = SQ_W_PER_TENSOR + SQ_STATIC_PER_TENSOR */
+typedef enum { SQ_W_PER_CHANNEL = 0, SQ_W_PER_TENSOR = 1 } sq_weight_mode;
 
 /*
  * sq_calibrate -- the offline half.
@@ -91,21 +107,26 @@ typedef enum { SQ_PER_TOKEN = 0, SQ_STATIC_PER_TENSOR = 1 } sq_act_mode;
  *   x_cal [T, K]  calibration activations (dtype x_dt: F32 or BF16), T >= 0
  *   w     [N, K]  weight, output channel x input channel (F32 or BF16), N >= 0
  *   alpha         migration strength in [0, 1]
+ *   w_mode        SQ_W_PER_CHANNEL or SQ_W_PER_TENSOR ([Review] §6.3)
  *   ln_gamma, ln_beta [K] fp32: the LayerNorm in front of the layer, or both
  *                 NULL when there is none
  * Outputs (device, caller-owned):
  *   s [K] fp32            smoothing factor
  *   wq [N, K] int8        smoothed, quantized weight
- *   w_scale [N] fp32      dw_n per output channel
+ *   w_scale               [N] fp32 dw_n per output channel (SQ_W_PER_CHANNEL), or
+ *                         [1] fp32 dw (SQ_W_PER_TENSOR)
  *   act_scale_static [1]  dx_static (may be NULL)
  *   ln_gamma_s, ln_beta_s [K] fp32: folded LayerNorm (required iff ln_gamma)
  *   x_absmax, w_absmax [K] fp32: a_j and w_j (required; they also serve as the
  *                 library's working memory for the two column maxima)
- * Kernels: a fill of the maxima, two column-absmax passes, the factor pass,
- * one weight smooth+quantize pass.  Reads X_cal and W once each from HBM.
+ * Kernels: the column-absmax pass over X_cal and W, the factor pass, one
+ * weight smooth+quantize pass; reads X_cal once and W twice.  SQ_W_PER_TENSOR
+ * adds a smoothed-row-maximum pass over W (staged in wq) and a one-block
+ * reduction before the quantize pass, which then uses the single step.
  */
 sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T,
                        const void* w, sq_dtype w_dt, int64_t N, int64_t K, float alpha,
+                       sq_weight_mode w_mode,
                        const float* ln_gamma, const float* ln_beta,
                        float* s, int8_t* wq, float* w_scale, float* act_scale_static,
                        float* ln_gamma_s, float* ln_beta_s,
@@ -124,8 +145,13 @@ sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T,
  *   mode      SQ_PER_TOKEN: x_scale [M] receives dx_t.
  *             SQ_STATIC_PER_TENSOR: static_scale [1] (device) holds dx_static;
  *             x_scale may be NULL and is not written.
+ *             SQ_DYNAMIC_PER_TENSOR ([Review] §6.3 O2): x_scale [1] receives
+ *             the batch step dx; static_scale is not read.
  *   xq [M, K] int8 output codes.
- * One kernel; reads X once and writes xq (and x_scale) once.
+ * Per-token and static: one kernel that reads X once and writes xq (and
+ * x_scale) once.  Dynamic per-tensor: a row-maximum pass (the maxima are
+ * staged in xq), a one-block reduction into x_scale[0], then the static
+ * quantizer with that step -- X is read twice.
  */
 sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
                                  const float* s, const float* ln_gamma_s,
@@ -140,14 +166,16 @@ sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_
  * (float)acc * (act_scale * weight_scale[n])); [Review] §2.6 / Fig. 3 (scales
  * only on the outer dimensions: token and output channel).
  *
- *   xq [M, K] int8, x_scale: [M] when x_mode = SQ_PER_TOKEN, [1] when static
- *   wq [N, K] int8, w_scale [N]
+ *   xq [M, K] int8, x_scale: [M] when x_mode = SQ_PER_TOKEN, [1] for either
+ *      per-tensor mode
+ *   wq [N, K] int8, w_scale: [N] when w_mode = SQ_W_PER_CHANNEL, [1] when
+ *      SQ_W_PER_TENSOR
  *   y  [M, N] of y_dt: SQ_F32, SQ_BF16, or SQ_I32 (the raw accumulators,
  *      x_scale and w_scale then unused and may be NULL)
  * Runs on the gfx950 int8 matrix cores (MFMA), LDS-staged K tiles.
  */
 sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_mode x_mode,
-                       const int8_t* wq, const float* w_scale,
+                       const int8_t* wq, const float* w_scale, sq_weight_mode w_mode,
                        int64_t M, int64_t N, int64_t K,
                        void* y, sq_dtype y_dt, sq_stream_t stream);
 

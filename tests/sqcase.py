@@ -45,12 +45,12 @@ def sample_idx(n: int, k: int, seed: int) -> np.ndarray:
     return np.sort(np.concatenate([[0, n - 1], mid])).astype(np.int64)
 
 
-def gpu_calibrate(x_cal, w, alpha, gamma=None, beta=None):
+def gpu_calibrate(x_cal, w, alpha, gamma=None, beta=None, w_mode="per_channel"):
     d = dev()
     xt, wt = to_dev(x_cal, d), to_dev(w, d)
     gt = None if gamma is None else to_dev(gamma, d)
     bt = None if beta is None else to_dev(beta, d)
-    out = sq.sq_calibrate(xt, wt, alpha, gt, bt)
+    out = sq.sq_calibrate(xt, wt, alpha, gt, bt, w_mode=w_mode)
     del xt
     return out, wt
 
@@ -73,17 +73,23 @@ def assert_same(name, gpu, ref):
 
 def run_layer(spec: datagen.LayerSpec, x_cal, w, x, mode: str, n_rows: int | None = None,
               n_cols: int | None = None, seed: int = 0, out_kinds=("bf16", "f32", "i32"),
-              gamma=None, beta=None, alpha=None):
+              gamma=None, beta=None, alpha=None, w_mode="per_channel"):
     """Run the whole path on the GPU and compare with the oracle.
 
+    mode: activation step "per_token" | "static" | "dynamic_per_tensor";
+    w_mode: weight step "per_channel" | "per_tensor".
     n_rows / n_cols: sample sizes of tokens / output channels for the
-    element-wise comparison of per-row outputs (None = all)."""
+    element-wise comparison of per-row outputs (None = all).  The per-tensor
+    steps need every row, so the oracle then quantizes in full and the
+    comparison samples."""
     alpha = spec.alpha if alpha is None else alpha
     M, K = x.shape
     N = w.shape[0]
-    say(f"[case] {spec.name} M={M} N={N} K={K} alpha={alpha} mode={mode} ln={spec.ln}")
+    wpt = w_mode == "per_tensor"
+    say(f"[case] {spec.name} M={M} N={N} K={K} alpha={alpha} mode={mode} w_mode={w_mode} "
+        f"ln={spec.ln}")
     # ---- GPU
-    cal, wt = gpu_calibrate(x_cal, w, alpha, gamma, beta)
+    cal, wt = gpu_calibrate(x_cal, w, alpha, gamma, beta, w_mode=w_mode)
     d = dev()
     xt = to_dev(x, d)
     if spec.ln:
@@ -92,7 +98,8 @@ def run_layer(spec: datagen.LayerSpec, x_cal, w, x, mode: str, n_rows: int | Non
     else:
         xq_t, xs_t = sq.sq_smooth_quantize_act(xt, cal["s"], mode=mode,
                                                static_scale=cal["static_scale"])
-    ys = {k: sq.sq_gemm_w8a8(xq_t, xs_t, cal["wq"], cal["w_scale"], mode, k) for k in out_kinds}
+    ys = {k: sq.sq_gemm_w8a8(xq_t, xs_t, cal["wq"], cal["w_scale"], mode, k, w_mode=w_mode)
+          for k in out_kinds}
     torch.cuda.synchronize()
     say("  gpu done")
 
@@ -113,31 +120,44 @@ def run_layer(spec: datagen.LayerSpec, x_cal, w, x, mode: str, n_rows: int | Non
 
     cols = None if n_cols is None else sample_idx(N, n_cols, seed + 1)
     rows = None if n_rows is None else sample_idx(M, n_rows, seed + 2)
-    wq_o, wsc_o = oracle.weight_quant(w, s, rows=cols)
     wq_g = to_np(cal["wq"])
     wsc_g = to_np(cal["w_scale"])
+    if wpt:
+        wq_o, wsc_o = oracle.weight_quant_per_tensor(w, s)
+        if cols is not None:
+            wq_o = wq_o[cols]
+    else:
+        wq_o, wsc_o = oracle.weight_quant(w, s, rows=cols)
+        if cols is not None:
+            wsc_g = wsc_g[cols]
     if cols is not None:
-        wq_g, wsc_g = wq_g[cols], wsc_g[cols]
+        wq_g = wq_g[cols]
     assert_same("w_scale", wsc_g, wsc_o)
     assert_same("wq", wq_g, wq_o)
 
     static = st if mode == "static" else None
+    dyn_t = mode == "dynamic_per_tensor"
+    act_rows = None if dyn_t else rows
     if spec.ln:
-        xq_o, xs_o, sat = oracle.smooth_quantize_act(x, g_s=gs, b_s=bs, static=static, rows=rows)
+        xq_o, xs_o, sat = oracle.smooth_quantize_act(x, g_s=gs, b_s=bs, static=static,
+                                                     rows=act_rows, dynamic_per_tensor=dyn_t)
     else:
-        xq_o, xs_o, sat = oracle.smooth_quantize_act(x, s=s, static=static, rows=rows)
+        xq_o, xs_o, sat = oracle.smooth_quantize_act(x, s=s, static=static, rows=act_rows,
+                                                     dynamic_per_tensor=dyn_t)
+    if dyn_t and rows is not None:
+        xq_o = xq_o[rows]
     xq_g = to_np(xq_t)
     xs_g = to_np(xs_t)
     if rows is not None:
         xq_g = xq_g[rows]
-        if mode != "static":
+        if mode == "per_token":
             xs_g = xs_g[rows]
     assert_same("xq", xq_g, xq_o)
     assert_same("x_scale", xs_g, xs_o)
 
     acc = oracle.gemm_i32(xq_o, wq_o)
-    per_token = mode != "static"
-    y32 = oracle.dequant(acc, xs_o, wsc_o, per_token=per_token)
+    per_token = mode == "per_token"
+    y32 = oracle.dequant(acc, xs_o, wsc_o, per_token=per_token, w_per_tensor=wpt)
     refs = {"i32": acc, "f32": y32, "bf16": oracle.f32_to_bf16(y32)}
     for k, yt in ys.items():
         yg = to_np(yt)

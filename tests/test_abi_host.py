@@ -51,8 +51,8 @@ def test_status_strings():
     assert L.sq_status_string(99).decode() == "SQ_ERR_UNKNOWN"
 
 
-def _gemm(M=4, N=4, K=64, xq=P, xs=P, mode=0, wq=P, ws=P, y=P, ydt=0):
-    return sq.lib().sq_gemm_w8a8(xq, xs, mode, wq, ws, M, N, K, y, ydt, None)
+def _gemm(M=4, N=4, K=64, xq=P, xs=P, mode=0, wq=P, ws=P, wmode=0, y=P, ydt=0):
+    return sq.lib().sq_gemm_w8a8(xq, xs, mode, wq, ws, wmode, M, N, K, y, ydt, None)
 
 
 def _act(M=4, K=64, x=P, dt=1, s=P, g=None, b=None, eps=1e-5, mode=0, st=None, xq=P, xs=P):
@@ -60,9 +60,9 @@ def _act(M=4, K=64, x=P, dt=1, s=P, g=None, b=None, eps=1e-5, mode=0, st=None, x
 
 
 def _cal(T=8, N=8, K=64, alpha=0.5, xdt=1, wdt=1, g=None, b=None, gs=None, bs=None, x=P, w=P,
-         s=P, wq=P, wsc=P, st=P, xa=P, wa=P):
-    return sq.lib().sq_calibrate(x, xdt, T, w, wdt, N, K, alpha, g, b, s, wq, wsc, st, gs, bs,
-                                 xa, wa, None)
+         s=P, wq=P, wsc=P, st=P, xa=P, wa=P, wmode=0):
+    return sq.lib().sq_calibrate(x, xdt, T, w, wdt, N, K, alpha, wmode, g, b, s, wq, wsc, st, gs,
+                                 bs, xa, wa, None)
 
 
 @pytest.mark.parametrize("K", [0, -64, 63, 65, 100, sq.SQ_MAX_K + 64])
@@ -76,6 +76,8 @@ def test_gemm_validation():
     assert _gemm(ydt=7) == 3
     assert _gemm(ydt=2) == 3          # int8 output is not an output type
     assert _gemm(mode=5) == 7
+    assert _gemm(wmode=2) == 7
+    assert _gemm(wmode=-1) == 7
     assert _gemm(xq=None) == 1
     assert _gemm(wq=None) == 1
     assert _gemm(y=None) == 1
@@ -92,7 +94,8 @@ def test_act_validation():
     assert _act(K=96) == 2
     assert _act(M=-3) == 2
     assert _act(dt=2) == 3
-    assert _act(mode=2) == 7
+    assert _act(mode=3) == 7
+    assert _act(mode=2, xs=None) == 1                  # dynamic per-tensor writes its step
     assert _act(s=None) == 1                           # neither plain nor LN
     assert _act(g=P, b=P) == 7                         # both plain and LN
     assert _act(s=None, g=P, b=None) == 1              # half of LN
@@ -121,6 +124,9 @@ def test_calibrate_validation():
     assert _cal(g=P, b=None) == 7                      # gamma without beta
     assert _cal(g=P, b=P, gs=None, bs=P) == 1          # fold outputs required
     assert _cal(wsc=MIS) == 5
+    assert _cal(wmode=2) == 7
+    assert _cal(wmode=1, wsc=None) == 1                # the per-tensor step is an output
+    assert _cal(wmode=1, N=0, w=None, wq=None, wsc=None) == 1
 
 
 def test_binding_rejects_cpu_tensors():

@@ -26,9 +26,20 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsq.so")
 
 SQ_F32, SQ_BF16, SQ_I8, SQ_I32 = 0, 1, 2, 3
-SQ_PER_TOKEN, SQ_STATIC_PER_TENSOR = 0, 1
+SQ_PER_TOKEN, SQ_STATIC_PER_TENSOR, SQ_DYNAMIC_PER_TENSOR = 0, 1, 2
+SQ_W_PER_CHANNEL, SQ_W_PER_TENSOR = 0, 1
 SQ_MAX_K = 133120
-SQ_ABI_VERSION = 1
+SQ_ABI_VERSION = 2
+
+# The SmoothQuant efficiency levels ([Review] §6.3): (weight mode, activation
+# mode).  "colwise" is the per-output-channel weight path with per-token
+# activations.
+SETTINGS = {
+    "colwise": ("per_channel", "per_token"),
+    "O1": ("per_tensor", "per_token"),
+    "O2": ("per_tensor", "dynamic_per_tensor"),
+    "O3": ("per_tensor", "static"),
+}
 EXPORTED = ("sq_calibrate", "sq_smooth_quantize_act", "sq_gemm_w8a8", "sq_status_string",
             "sq_abi_version")
 
@@ -51,12 +62,12 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, ci, cf = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     L.sq_calibrate.restype = ci
-    L.sq_calibrate.argtypes = [vp, ci, i64, vp, ci, i64, i64, cf, vp, vp, vp, vp, vp, vp, vp, vp,
-                               vp, vp, vp]
+    L.sq_calibrate.argtypes = [vp, ci, i64, vp, ci, i64, i64, cf, ci, vp, vp, vp, vp, vp, vp, vp,
+                               vp, vp, vp, vp]
     L.sq_smooth_quantize_act.restype = ci
     L.sq_smooth_quantize_act.argtypes = [vp, ci, i64, i64, vp, vp, vp, cf, ci, vp, vp, vp, vp]
     L.sq_gemm_w8a8.restype = ci
-    L.sq_gemm_w8a8.argtypes = [vp, vp, ci, vp, vp, i64, i64, i64, vp, ci, vp]
+    L.sq_gemm_w8a8.argtypes = [vp, vp, ci, vp, vp, ci, i64, i64, i64, vp, ci, vp]
     L.sq_status_string.restype = ctypes.c_char_p
     L.sq_status_string.argtypes = [ci]
     L.sq_abi_version.restype = ci
@@ -100,14 +111,26 @@ def _mode(mode) -> int:
         return SQ_PER_TOKEN
     if mode in ("static", SQ_STATIC_PER_TENSOR):
         return SQ_STATIC_PER_TENSOR
+    if mode in ("dynamic_per_tensor", SQ_DYNAMIC_PER_TENSOR):
+        return SQ_DYNAMIC_PER_TENSOR
     raise ValueError(f"unknown activation mode {mode!r}")
+
+
+def _wmode(mode) -> int:
+    if mode in ("per_channel", SQ_W_PER_CHANNEL):
+        return SQ_W_PER_CHANNEL
+    if mode in ("per_tensor", SQ_W_PER_TENSOR):
+        return SQ_W_PER_TENSOR
+    raise ValueError(f"unknown weight mode {mode!r}")
 
 
 def sq_calibrate(x_cal: torch.Tensor, w: torch.Tensor, alpha: float,
                  ln_gamma: torch.Tensor | None = None, ln_beta: torch.Tensor | None = None,
-                 out: dict | None = None) -> dict:
+                 out: dict | None = None, w_mode="per_channel") -> dict:
     """Offline half: returns dict(s, wq, w_scale, static_scale, x_absmax, w_absmax
-    [, ln_gamma_s, ln_beta_s]).  ``out`` may supply preallocated tensors."""
+    [, ln_gamma_s, ln_beta_s]).  ``out`` may supply preallocated tensors.
+    w_mode "per_channel" (w_scale [N]) or "per_tensor" (w_scale [1])."""
+    wm = _wmode(w_mode)
     _dev2d(x_cal, "x_cal")
     _dev2d(w, "w")
     T, K = x_cal.shape
@@ -119,7 +142,7 @@ def sq_calibrate(x_cal: torch.Tensor, w: torch.Tensor, alpha: float,
     f32 = dict(dtype=torch.float32, device=dev)
     o.setdefault("s", torch.empty(K, **f32))
     o.setdefault("wq", torch.empty((N, K), dtype=torch.int8, device=dev))
-    o.setdefault("w_scale", torch.empty(N, **f32))
+    o.setdefault("w_scale", torch.empty(N if wm == SQ_W_PER_CHANNEL else 1, **f32))
     o.setdefault("static_scale", torch.empty(1, **f32))
     o.setdefault("x_absmax", torch.empty(K, **f32))
     o.setdefault("w_absmax", torch.empty(K, **f32))
@@ -127,7 +150,7 @@ def sq_calibrate(x_cal: torch.Tensor, w: torch.Tensor, alpha: float,
         o.setdefault("ln_gamma_s", torch.empty(K, **f32))
         o.setdefault("ln_beta_s", torch.empty(K, **f32))
     _check(lib().sq_calibrate(
-        _ptr(x_cal), _dt(x_cal), T, _ptr(w), _dt(w), N, K, float(alpha),
+        _ptr(x_cal), _dt(x_cal), T, _ptr(w), _dt(w), N, K, float(alpha), wm,
         _ptr(ln_gamma), _ptr(ln_beta), _ptr(o["s"]), _ptr(o["wq"]), _ptr(o["w_scale"]),
         _ptr(o["static_scale"]), _ptr(o.get("ln_gamma_s")), _ptr(o.get("ln_beta_s")),
         _ptr(o["x_absmax"]), _ptr(o["w_absmax"]), _stream(dev)))
@@ -139,20 +162,22 @@ def sq_smooth_quantize_act(x: torch.Tensor, s: torch.Tensor | None = None,
                            ln_beta_s: torch.Tensor | None = None, ln_eps: float = 1e-5,
                            mode="per_token", static_scale: torch.Tensor | None = None,
                            xq: torch.Tensor | None = None, x_scale: torch.Tensor | None = None):
-    """Runtime activation side: returns (xq int8 [M,K], x_scale fp32 [M] or the
-    static scale [1])."""
+    """Runtime activation side: returns (xq int8 [M,K], the step(s)): x_scale
+    fp32 [M] per token, the batch step [1] for "dynamic_per_tensor", or the
+    static scale [1]."""
     _dev2d(x, "x")
     M, K = x.shape
     md = _mode(mode)
     if xq is None:
         xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    if md == SQ_PER_TOKEN and x_scale is None:
-        x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    if md != SQ_STATIC_PER_TENSOR and x_scale is None:
+        n = M if md == SQ_PER_TOKEN else 1
+        x_scale = torch.empty(n, dtype=torch.float32, device=x.device)
     _check(lib().sq_smooth_quantize_act(
         _ptr(x), _dt(x), M, K, _ptr(s), _ptr(ln_gamma_s), _ptr(ln_beta_s), float(ln_eps), md,
-        _ptr(static_scale), _ptr(xq), _ptr(x_scale) if md == SQ_PER_TOKEN else None,
-        _stream(x.device)))
-    return xq, (x_scale if md == SQ_PER_TOKEN else static_scale)
+        _ptr(static_scale) if md == SQ_STATIC_PER_TENSOR else None, _ptr(xq),
+        _ptr(x_scale) if md != SQ_STATIC_PER_TENSOR else None, _stream(x.device)))
+    return xq, (static_scale if md == SQ_STATIC_PER_TENSOR else x_scale)
 
 
 _OUT = {"f32": (SQ_F32, torch.float32), "bf16": (SQ_BF16, torch.bfloat16),
@@ -161,8 +186,9 @@ _OUT = {"f32": (SQ_F32, torch.float32), "bf16": (SQ_BF16, torch.bfloat16),
 
 def sq_gemm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor,
                  w_scale: torch.Tensor | None, mode="per_token", out_dtype: str = "bf16",
-                 y: torch.Tensor | None = None) -> torch.Tensor:
-    """Int8 GEMM + dequant: y[M,N] = RN(float(acc) * RN(dx_t * dw_n))."""
+                 y: torch.Tensor | None = None, w_mode="per_channel") -> torch.Tensor:
+    """Int8 GEMM + dequant: y[M,N] = RN(float(acc) * RN(dx_t * dw_n)); mode is
+    the activation step granularity, w_mode the weight's."""
     _dev2d(xq, "xq")
     _dev2d(wq, "wq")
     M, K = xq.shape
@@ -173,5 +199,5 @@ def sq_gemm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tenso
     if y is None:
         y = torch.empty((M, N), dtype=tdt, device=xq.device)
     _check(lib().sq_gemm_w8a8(_ptr(xq), _ptr(x_scale), _mode(mode), _ptr(wq), _ptr(w_scale),
-                              M, N, K, _ptr(y), code, _stream(xq.device)))
+                              _wmode(w_mode), M, N, K, _ptr(y), code, _stream(xq.device)))
     return y

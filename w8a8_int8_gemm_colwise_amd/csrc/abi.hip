@@ -25,16 +25,18 @@ sq_status from_hip(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; 
 extern "C" {
 
 sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T, const void* w, sq_dtype w_dt,
-                       int64_t N, int64_t K, float alpha, const float* ln_gamma,
-                       const float* ln_beta, float* s, int8_t* wq, float* w_scale,
-                       float* act_scale_static, float* ln_gamma_s, float* ln_beta_s,
-                       float* x_absmax, float* w_absmax, sq_stream_t stream) {
+                       int64_t N, int64_t K, float alpha, sq_weight_mode w_mode,
+                       const float* ln_gamma, const float* ln_beta, float* s, int8_t* wq,
+                       float* w_scale, float* act_scale_static, float* ln_gamma_s,
+                       float* ln_beta_s, float* x_absmax, float* w_absmax, sq_stream_t stream) {
     if (!valid_k(K) || !valid_rows(T) || !valid_rows(N)) return SQ_ERR_BAD_SHAPE;
     if (!float_dtype(x_dt) || !float_dtype(w_dt)) return SQ_ERR_BAD_DTYPE;
     if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_BAD_ALPHA;
+    if (w_mode != SQ_W_PER_CHANNEL && w_mode != SQ_W_PER_TENSOR) return SQ_ERR_BAD_MODE;
     if (!s || !x_absmax || !w_absmax) return SQ_ERR_NULL_ARG;
     if (T > 0 && !x_cal) return SQ_ERR_NULL_ARG;
-    if (N > 0 && (!w || !wq || !w_scale)) return SQ_ERR_NULL_ARG;
+    if (N > 0 && (!w || !wq)) return SQ_ERR_NULL_ARG;
+    if ((N > 0 || w_mode == SQ_W_PER_TENSOR) && !w_scale) return SQ_ERR_NULL_ARG;
     if ((ln_gamma == nullptr) != (ln_beta == nullptr)) return SQ_ERR_BAD_MODE;
     if (ln_gamma && (!ln_gamma_s || !ln_beta_s)) return SQ_ERR_NULL_ARG;
     const void* ptrs[] = {x_cal, w, ln_gamma, ln_beta, s, wq, w_scale, act_scale_static,
@@ -42,7 +44,8 @@ sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T, const void* 
     for (const void* p : ptrs)
         if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
     return from_hip(sq::launch_calibrate(
-        x_cal, to_dt(x_dt), T, w, to_dt(w_dt), N, K, alpha, ln_gamma, ln_beta, s, wq, w_scale,
+        x_cal, to_dt(x_dt), T, w, to_dt(w_dt), N, K, alpha, w_mode == SQ_W_PER_TENSOR, ln_gamma,
+        ln_beta, s, wq, w_scale,
         act_scale_static, ln_gamma ? ln_gamma_s : nullptr, ln_gamma ? ln_beta_s : nullptr,
         x_absmax, w_absmax, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -54,7 +57,8 @@ sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_
                                  sq_stream_t stream) {
     if (!valid_k(K) || !valid_rows(M)) return SQ_ERR_BAD_SHAPE;
     if (!float_dtype(x_dt)) return SQ_ERR_BAD_DTYPE;
-    if (mode != SQ_PER_TOKEN && mode != SQ_STATIC_PER_TENSOR) return SQ_ERR_BAD_MODE;
+    if (mode != SQ_PER_TOKEN && mode != SQ_STATIC_PER_TENSOR && mode != SQ_DYNAMIC_PER_TENSOR)
+        return SQ_ERR_BAD_MODE;
     const bool ln = (ln_gamma_s != nullptr) || (ln_beta_s != nullptr);
     if (ln) {
         if (s) return SQ_ERR_BAD_MODE;
@@ -65,23 +69,29 @@ sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_
     }
     if (mode == SQ_STATIC_PER_TENSOR && !static_scale) return SQ_ERR_NULL_ARG;
     if (M > 0 && (!x || !xq)) return SQ_ERR_NULL_ARG;
-    if (M > 0 && mode == SQ_PER_TOKEN && !x_scale) return SQ_ERR_NULL_ARG;
-    const void* ptrs[] = {x, s, ln_gamma_s, ln_beta_s, static_scale, xq, x_scale};
+    if (M > 0 && mode != SQ_STATIC_PER_TENSOR && !x_scale) return SQ_ERR_NULL_ARG;
+    const float* st = (mode == SQ_STATIC_PER_TENSOR) ? static_scale : nullptr;
+    const void* ptrs[] = {x, s, ln_gamma_s, ln_beta_s, st, xq, x_scale};
     for (const void* p : ptrs)
         if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
+    const sq::ActMode am = mode == SQ_PER_TOKEN           ? sq::ActMode::PerToken
+                           : mode == SQ_STATIC_PER_TENSOR ? sq::ActMode::Static
+                                                          : sq::ActMode::DynamicTensor;
     return from_hip(sq::launch_act_quant(x, to_dt(x_dt), M, K, ln ? nullptr : s, ln_gamma_s,
-                                         ln_beta_s, ln_eps, mode == SQ_STATIC_PER_TENSOR,
-                                         static_scale, xq, x_scale,
+                                         ln_beta_s, ln_eps, am, st, xq, x_scale,
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
 sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_mode x_mode,
-                       const int8_t* wq, const float* w_scale, int64_t M, int64_t N, int64_t K,
-                       void* y, sq_dtype y_dt, sq_stream_t stream) {
+                       const int8_t* wq, const float* w_scale, sq_weight_mode w_mode, int64_t M,
+                       int64_t N, int64_t K, void* y, sq_dtype y_dt, sq_stream_t stream) {
     if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return SQ_ERR_BAD_SHAPE;
     if (M * N > (int64_t(1) << 40)) return SQ_ERR_BAD_SHAPE;
     if (y_dt != SQ_F32 && y_dt != SQ_BF16 && y_dt != SQ_I32) return SQ_ERR_BAD_DTYPE;
-    if (x_mode != SQ_PER_TOKEN && x_mode != SQ_STATIC_PER_TENSOR) return SQ_ERR_BAD_MODE;
+    if (x_mode != SQ_PER_TOKEN && x_mode != SQ_STATIC_PER_TENSOR &&
+        x_mode != SQ_DYNAMIC_PER_TENSOR)
+        return SQ_ERR_BAD_MODE;
+    if (w_mode != SQ_W_PER_CHANNEL && w_mode != SQ_W_PER_TENSOR) return SQ_ERR_BAD_MODE;
     if (M > 0 && N > 0) {
         if (!xq || !wq || !y) return SQ_ERR_NULL_ARG;
         if (y_dt != SQ_I32 && (!x_scale || !w_scale)) return SQ_ERR_NULL_ARG;
@@ -90,8 +100,9 @@ sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_mode x_mod
     for (const void* p : ptrs)
         if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
     const int out = (y_dt == SQ_F32) ? 0 : (y_dt == SQ_BF16) ? 1 : 2;
-    return from_hip(sq::launch_gemm(xq, x_scale, x_mode == SQ_PER_TOKEN, wq, w_scale, M, N, K,
-                                    y, out, reinterpret_cast<hipStream_t>(stream)));
+    return from_hip(sq::launch_gemm(xq, x_scale, x_mode == SQ_PER_TOKEN, wq, w_scale,
+                                    w_mode == SQ_W_PER_TENSOR, M, N, K, y, out,
+                                    reinterpret_cast<hipStream_t>(stream)));
 }
 
 const char* sq_status_string(sq_status status) {

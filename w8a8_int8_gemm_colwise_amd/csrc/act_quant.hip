@@ -81,12 +81,15 @@ __device__ __forceinline__ int quantize(float xh, float d, float rd) {
 // current row is reduced and quantized (a ring of D+1 rows of 16-byte chunks).
 // D = 0: the constants are re-read per row (L2 hits), 1/s_k is an IEEE
 // division, and nothing is prefetched.
+// rowmax != nullptr (dynamic modes only): the row pass that stores the raw
+// maximum max_k |xh_k| of every row in rowmax[m] and writes neither codes nor
+// x_scale -- the first pass of the dynamic per-tensor step.
 template <typename T, bool LN, bool STATIC, int CPT, int D, int MAXT>
 __global__ __launch_bounds__(MAXT) void act_quant_kernel(
     const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
     const float* __restrict__ gs, const float* __restrict__ bs, float eps,
     const float* __restrict__ static_scale, int8_t* __restrict__ xq,
-    float* __restrict__ x_scale) {
+    float* __restrict__ x_scale, float* __restrict__ rowmax) {
     __shared__ float lds[kLnThreads + 4];
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
@@ -226,17 +229,22 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
             mx = block_max(mx, lds);
             d = step_from_absmax(mx);
             rd = 1.0f / d;
-            if (tid == 0) x_scale[m] = d;
+            if (tid == 0) {
+                if (rowmax) rowmax[m] = mx;
+                else x_scale[m] = d;
+            }
         }
-        int8_t* orow = xq + m * K;
+        if (STATIC || rowmax == nullptr) {
+            int8_t* orow = xq + m * K;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
-            if (c < chunks) {
-                int q[kChunk];
+            for (int i = 0; i < CPT; ++i) {
+                const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+                if (c < chunks) {
+                    int q[kChunk];
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[i][e], d, rd);
-                *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
+                    for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[i][e], d, rd);
+                    *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
+                }
             }
         }
 #pragma unroll
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_stream_kernel(
     const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
     const float* __restrict__ gs, const float* __restrict__ bs, float eps,
     const float* __restrict__ static_scale, int8_t* __restrict__ xq,
-    float* __restrict__ x_scale) {
+    float* __restrict__ x_scale, float* __restrict__ rowmax) {
     __shared__ float lds[kLnThreads + 4];
     const int tid = threadIdx.x;
     const int64_t chunks = K / kChunk;
@@ -321,6 +329,10 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_stream_kernel(
             }
             mx = block_max(mx, lds);
             d = step_from_absmax(mx);
+            if (rowmax) {
+                if (tid == 0) rowmax[m] = mx;
+                continue;
+            }
             if (tid == 0) x_scale[m] = d;
         }
         rd = 1.0f / d;
@@ -343,6 +355,7 @@ struct ActArgs {
     const float* static_scale;
     int8_t* xq;
     float* x_scale;
+    float* rowmax;  // non-null: row-maximum pass (dynamic per-tensor step)
 };
 
 template <typename T, bool LN, bool STATIC, int CPT, int D, int MAXT = 1024>
@@ -352,7 +365,7 @@ hipError_t run(const ActArgs& a, int threads, hipStream_t stream) {
     const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.M, 256 * per_cu));
     act_quant_kernel<T, LN, STATIC, CPT, D, MAXT><<<grid, threads, 0, stream>>>(
         static_cast<const T*>(a.x), a.M, a.K, a.s, a.gs, a.bs, a.eps, a.static_scale, a.xq,
-        a.x_scale);
+        a.x_scale, a.rowmax);
     return hipGetLastError();
 }
 
@@ -361,7 +374,7 @@ hipError_t run_stream(const ActArgs& a, hipStream_t stream) {
     const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.M, 2048));
     act_quant_stream_kernel<T, LN, STATIC><<<grid, kLnThreads, 0, stream>>>(
         static_cast<const T*>(a.x), a.M, a.K, a.s, a.gs, a.bs, a.eps, a.static_scale, a.xq,
-        a.x_scale);
+        a.x_scale, a.rowmax);
     return hipGetLastError();
 }
 
@@ -403,13 +416,30 @@ hipError_t dispatch(const ActArgs& a, bool ln, bool st, hipStream_t stream) {
 
 hipError_t launch_act_quant(const void* x, Dt x_dt, int64_t M, int64_t K, const float* s,
                             const float* gamma_s, const float* beta_s, float eps,
-                            bool static_mode, const float* static_scale, int8_t* xq,
+                            ActMode mode, const float* static_scale, int8_t* xq,
                             float* x_scale, hipStream_t stream) {
-    if (M <= 0) return hipSuccess;
-    const ActArgs a{x, M, K, s, gamma_s, beta_s, eps, static_scale, xq, x_scale};
+    if (M <= 0) {
+        // an empty batch: the dynamic per-tensor step is FLOOR / 127
+        return mode == ActMode::DynamicTensor ? launch_tensor_step(nullptr, 0, x_scale, stream)
+                                              : hipSuccess;
+    }
     const bool ln = (s == nullptr);
-    return (x_dt == Dt::BF16) ? dispatch<uint16_t>(a, ln, static_mode, stream)
-                              : dispatch<float>(a, ln, static_mode, stream);
+    auto go = [&](const ActArgs& a, bool st) {
+        return (x_dt == Dt::BF16) ? dispatch<uint16_t>(a, ln, st, stream)
+                                  : dispatch<float>(a, ln, st, stream);
+    };
+    if (mode != ActMode::DynamicTensor)
+        return go(ActArgs{x, M, K, s, gamma_s, beta_s, eps, static_scale, xq, x_scale, nullptr},
+                  mode == ActMode::Static);
+    // dynamic per tensor: row maxima (staged in xq, 4M <= M*K bytes), the
+    // one-block reduction into x_scale[0], then the static quantizer with it
+    float* rowmax = reinterpret_cast<float*>(xq);
+    hipError_t e = go(ActArgs{x, M, K, s, gamma_s, beta_s, eps, nullptr, xq, nullptr, rowmax},
+                      false);
+    if (e != hipSuccess) return e;
+    e = launch_tensor_step(rowmax, M, x_scale, stream);
+    if (e != hipSuccess) return e;
+    return go(ActArgs{x, M, K, s, gamma_s, beta_s, eps, x_scale, xq, nullptr, nullptr}, true);
 }
 
 }  // namespace sq

@@ -282,7 +282,13 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
 // row the block walks, and the loads of the block's next D rows are in flight
 // while the current row is reduced and quantized (a ring of D+1 rows).  The
 // row stays in registers between the absmax and the quantize passes.
-template <typename T, int CPT, int D, int MAXT = 1024>
+// What the weight kernels produce per row n (the third argument `ws`):
+//   kWChannel  step dw_n = RN(max(FLOOR, max_k |What|) / 127) into ws[n], codes
+//   kWRowMax   the raw maximum max_k |What| into ws[n] (float scratch), no codes
+//   kWGiven    codes with the step read from ws[0] (per-tensor), ws not written
+enum WMode : int { kWChannel = 0, kWRowMax = 1, kWGiven = 2 };
+
+template <typename T, int CPT, int D, int MAXT = 1024, int WM = kWChannel>
 __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
     const T* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,
     int8_t* __restrict__ wq, float* __restrict__ w_scale) {
@@ -293,6 +299,8 @@ __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
     const int64_t chunks = K / kChunk;
     const int64_t G = gridDim.x;
     constexpr bool CACHE = D > 0;
+    const float d_given = (WM == kWGiven) ? w_scale[0] : 0.0f;
+    const float rd_given = (WM == kWGiven) ? 1.0f / d_given : 0.0f;
 
     RawChunk<T> ring[D + 1][CPT];
     auto fetch = [&](int64_t n, RawChunk<T> (&r)[CPT]) {
@@ -337,26 +345,31 @@ __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
                 }
             }
         }
-        m = wave_max(m);
-        if (nw > 1) {
-            if ((tid & 63) == 0) red[tid >> 6] = m;
-            __syncthreads();
-            m = red[0];
-            for (int i = 1; i < nw; ++i) m = fmaxf(m, red[i]);
-            __syncthreads();  // red is reused by the next row
+        float d = d_given, rd = rd_given;
+        if (WM != kWGiven) {
+            m = wave_max(m);
+            if (nw > 1) {
+                if ((tid & 63) == 0) red[tid >> 6] = m;
+                __syncthreads();
+                m = red[0];
+                for (int i = 1; i < nw; ++i) m = fmaxf(m, red[i]);
+                __syncthreads();  // red is reused by the next row
+            }
+            d = step_from_absmax(m);
+            rd = 1.0f / d;
+            if (tid == 0) w_scale[n] = (WM == kWRowMax) ? m : d;
         }
-        const float d = step_from_absmax(m);
-        const float rd = 1.0f / d;
-        if (tid == 0) w_scale[n] = d;
-        int8_t* orow = wq + n * K;
+        if (WM != kWRowMax) {
+            int8_t* orow = wq + n * K;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
-            if (c < chunks) {
-                int q[kChunk];
+            for (int i = 0; i < CPT; ++i) {
+                const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+                if (c < chunks) {
+                    int q[kChunk];
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) q[e] = code_of(div_rn(v[i][e], d, rd));
-                *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
+                    for (int e = 0; e < kChunk; ++e) q[e] = code_of(div_rn(v[i][e], d, rd));
+                    *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
+                }
             }
         }
 #pragma unroll
@@ -367,31 +380,36 @@ __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
 }
 
 // Any K: two sweeps over the row from memory (the second mostly hits L2).
-template <typename T>
+template <typename T, int WM = kWChannel>
 __global__ __launch_bounds__(256) void weight_quant_stream_kernel(
     const T* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,
     int8_t* __restrict__ wq, float* __restrict__ w_scale) {
     __shared__ float red[4];
     const int tid = threadIdx.x;
     const int64_t chunks = K / kChunk;
+    const float d_given = (WM == kWGiven) ? w_scale[0] : 0.0f;
     for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
         const T* row = w + n * K;
-        float m = 0.0f;
-        for (int64_t c = tid; c < chunks; c += 256) {
-            float v[kChunk], sv[kChunk];
-            load_chunk(row, c, v);
-            load_chunk(s, c, sv);
+        float d = d_given;
+        if (WM != kWGiven) {
+            float m = 0.0f;
+            for (int64_t c = tid; c < chunks; c += 256) {
+                float v[kChunk], sv[kChunk];
+                load_chunk(row, c, v);
+                load_chunk(s, c, sv);
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) m = fmaxf(m, fabsf(v[e] * sv[e]));
+                for (int e = 0; e < kChunk; ++e) m = fmaxf(m, fabsf(v[e] * sv[e]));
+            }
+            m = wave_max(m);
+            if ((tid & 63) == 0) red[tid >> 6] = m;
+            __syncthreads();
+            m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            __syncthreads();
+            d = step_from_absmax(m);
+            if (tid == 0) w_scale[n] = (WM == kWRowMax) ? m : d;
+            if (WM == kWRowMax) continue;
         }
-        m = wave_max(m);
-        if ((tid & 63) == 0) red[tid >> 6] = m;
-        __syncthreads();
-        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        __syncthreads();
-        const float d = step_from_absmax(m);
         const float rd = 1.0f / d;
-        if (tid == 0) w_scale[n] = d;
         for (int64_t c = tid; c < chunks; c += 256) {
             float v[kChunk], sv[kChunk];
             load_chunk(row, c, v);
@@ -404,9 +422,9 @@ __global__ __launch_bounds__(256) void weight_quant_stream_kernel(
     }
 }
 
-template <typename T>
-hipError_t launch_weight_quant(const T* w, int64_t N, int64_t K, const float* s, int8_t* wq,
-                               float* w_scale, hipStream_t stream) {
+template <typename T, int WM>
+hipError_t launch_weight_quant_mode(const T* w, int64_t N, int64_t K, const float* s, int8_t* wq,
+                                    float* ws, hipStream_t stream) {
     if (N <= 0) return hipSuccess;
     const int64_t chunks = K / kChunk;
     // Measured on the MI355X: one prefetched row (D = 1) beats deeper rings, and
@@ -416,8 +434,8 @@ hipError_t launch_weight_quant(const T* w, int64_t N, int64_t K, const float* s,
     // lanes), longer ones the two-sweep kernel.
     if (chunks > 8 * 768) {
         const int64_t grid = std::min<int64_t>(N, 2048);
-        weight_quant_stream_kernel<T><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
-            w, N, K, s, wq, w_scale);
+        weight_quant_stream_kernel<T, WM><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
+            w, N, K, s, wq, ws);
         return hipGetLastError();
     }
     constexpr bool kBf16 = sizeof(T) == 2;
@@ -429,13 +447,44 @@ hipError_t launch_weight_quant(const T* w, int64_t N, int64_t K, const float* s,
     const int threads = std::max(64, round_up64((chunks + cpt - 1) / cpt));
     const int64_t per_cu = std::max(1, 1024 / threads);
     const unsigned g = static_cast<unsigned>(std::min<int64_t>(N, 256 * per_cu));
-    if (cpt == 1) weight_quant_kernel<T, 1, 1><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
-    else if (cpt == 2) weight_quant_kernel<T, 2, 1><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
-    else if (cpt == 4 && d == 1) weight_quant_kernel<T, kBf16 ? 4 : 2, 1><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
-    else if (cpt == 4) weight_quant_kernel<T, 4, 0><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
-    else weight_quant_kernel<T, 8, 0, 768><<<g, threads, 0, stream>>>(w, N, K, s, wq, w_scale);
+    if (cpt == 1) weight_quant_kernel<T, 1, 1, 1024, WM><<<g, threads, 0, stream>>>(w, N, K, s, wq, ws);
+    else if (cpt == 2) weight_quant_kernel<T, 2, 1, 1024, WM><<<g, threads, 0, stream>>>(w, N, K, s, wq, ws);
+    else if (cpt == 4 && d == 1) weight_quant_kernel<T, kBf16 ? 4 : 2, 1, 1024, WM><<<g, threads, 0, stream>>>(w, N, K, s, wq, ws);
+    else if (cpt == 4) weight_quant_kernel<T, 4, 0, 1024, WM><<<g, threads, 0, stream>>>(w, N, K, s, wq, ws);
+    else weight_quant_kernel<T, 8, 0, 768, WM><<<g, threads, 0, stream>>>(w, N, K, s, wq, ws);
     return hipGetLastError();
 }
+
+// Per output channel: one pass.  Per tensor: the smoothed row maxima (staged
+// as floats in wq, which only the last pass writes), the one-block reduction
+// into w_scale[0], then the codes with that single step.
+template <typename T>
+hipError_t launch_weight_quant(const T* w, int64_t N, int64_t K, const float* s, int8_t* wq,
+                               float* w_scale, bool per_tensor, hipStream_t stream) {
+    if (!per_tensor) return launch_weight_quant_mode<T, kWChannel>(w, N, K, s, wq, w_scale, stream);
+    float* rowmax = reinterpret_cast<float*>(wq);  // 4N bytes <= N*K bytes (K >= 64)
+    hipError_t e = launch_weight_quant_mode<T, kWRowMax>(w, N, K, s, wq, rowmax, stream);
+    if (e != hipSuccess) return e;
+    e = launch_tensor_step(rowmax, N, w_scale, stream);
+    if (e != hipSuccess) return e;
+    return launch_weight_quant_mode<T, kWGiven>(w, N, K, s, wq, w_scale, stream);
+}
+
+// One block: step[0] = RN(max(FLOOR, max_i m[i]) / 127) over non-negative maxima.
+__global__ __launch_bounds__(1024) void tensor_step_kernel(const float* __restrict__ m, int64_t n,
+                                                           float* __restrict__ step) {
+    __shared__ float red[16];
+    float v = 0.0f;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) v = fmaxf(v, m[i]);
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < 16; ++i) v = fmaxf(v, red[i]);
+        step[0] = step_from_absmax(v);
+    }
+}
+
 
 }  // namespace
 
@@ -473,8 +522,13 @@ hipError_t launch_partial(const TX* x, int64_t T, const TW* w, int64_t N, int64_
 
 }  // namespace
 
+hipError_t launch_tensor_step(const float* maxima, int64_t n, float* step, hipStream_t stream) {
+    tensor_step_kernel<<<1, 1024, 0, stream>>>(maxima, n, step);
+    return hipGetLastError();
+}
+
 hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w, Dt w_dt,
-                            int64_t N, int64_t K, float alpha, const float* gamma,
+                            int64_t N, int64_t K, float alpha, bool w_per_tensor, const float* gamma,
                             const float* beta, float* s, int8_t* wq, float* w_scale,
                             float* act_scale_static, float* gamma_s, float* beta_s,
                             float* x_absmax, float* w_absmax, hipStream_t stream) {
@@ -521,9 +575,15 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
+    if (N == 0) {
+        // no rows: the per-tensor step of an empty weight is FLOOR / 127
+        return w_per_tensor ? launch_tensor_step(nullptr, 0, w_scale, stream) : hipSuccess;
+    }
     return (w_dt == Dt::BF16)
-               ? launch_weight_quant(static_cast<const uint16_t*>(w), N, K, s, wq, w_scale, stream)
-               : launch_weight_quant(static_cast<const float*>(w), N, K, s, wq, w_scale, stream);
+               ? launch_weight_quant(static_cast<const uint16_t*>(w), N, K, s, wq, w_scale,
+                                     w_per_tensor, stream)
+               : launch_weight_quant(static_cast<const float*>(w), N, K, s, wq, w_scale,
+                                     w_per_tensor, stream);
 }
 
 }  // namespace sq

@@ -96,8 +96,8 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
 template <int OUT, int TM, int TN>
 __device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int row0, int col0, int lane,
                                            const float* __restrict__ sx, int sx_per_token,
-                                           const float* __restrict__ sw, void* __restrict__ Y,
-                                           int M, int N) {
+                                           const float* __restrict__ sw, int sw_per_tensor,
+                                           void* __restrict__ Y, int M, int N) {
     const int frow = lane & 31;
     const int fhalf = lane >> 5;
 #pragma unroll
@@ -118,7 +118,7 @@ __device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int row0, 
                     if (OUT == kOutI32) {
                         static_cast<int32_t*>(Y)[o] = a;
                     } else {
-                        const float f = dx * sw[col];
+                        const float f = dx * sw[sw_per_tensor ? 0 : col];
                         const float y = static_cast<float>(a) * f;
                         if (OUT == kOutF32)
                             static_cast<float*>(Y)[o] = y;
@@ -134,7 +134,8 @@ __device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int row0, 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
-    int sx_per_token, const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
+    int M, int N, int K) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     static_assert(T::LA * T::kThreads == BM * kChunksPerRow, "A tile divides over threads");
     static_assert(T::LB * T::kThreads == BN * kChunksPerRow, "B tile divides over threads");
@@ -234,28 +235,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     }
 
     store_tile<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + wn * T::WN, lane, sx, sx_per_token,
-                                  sw, Y, M, N);
+                                  sw, sw_per_tensor, Y, M, N);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
-               const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
+               const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, hipStream_t stream) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(tiles), block(T::kThreads);
     const int pt = per_token ? 1 : 0;
+    const int wpt = w_per_tensor ? 1 : 0;
     switch (out) {
         case kOutF32:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutF32><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, y, M, N, K);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K);
             break;
         case kOutBF16:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutBF16><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, y, M, N, K);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K);
             break;
         default:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutI32><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, y, M, N, K);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K);
             break;
     }
     return hipGetLastError();
@@ -405,7 +407,8 @@ __device__ __forceinline__ void dma16(const int8_t* base, uint32_t voff, uint32_
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OUT>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
-    int sx_per_token, const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
+    int M, int N, int K) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     static_assert(WAVES_M * WAVES_N == 8, "two groups of four waves");
     constexpr int kRows = BM + BN;
@@ -485,7 +488,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     float scale = 0.0f;
     const int st = threadIdx.x;
     if (OUT != kOutI32 && st < BM + BN)
-        scale = st < BM ? sx[sx_per_token ? min(m0 + st, M - 1) : 0] : sw[min(n0 + st - BM, N - 1)];
+        scale = st < BM ? sx[sx_per_token ? min(m0 + st, M - 1) : 0]
+                        : sw[sw_per_tensor ? 0 : min(n0 + st - BM, N - 1)];
     compiler_fence();
     for (int t = 0; t < STAGES - 1 && t < KT; ++t) issue(t);
     wait_stage(0);
@@ -534,22 +538,23 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
 hipError_t run_pp(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
-                  const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
+                  const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, hipStream_t stream) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(tiles), block(512);
     const int pt = per_token ? 1 : 0;
+    const int wpt = w_per_tensor ? 1 : 0;
     switch (out) {
         case kOutF32:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutF32>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
             break;
         case kOutBF16:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutBF16>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
             break;
         default:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutI32>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
             break;
     }
     return hipGetLastError();
@@ -593,7 +598,8 @@ __device__ __forceinline__ void skinny_issue(const int8_t* A, const int8_t* B, c
 template <int MT, int WPB, int ST, int OUT>
 __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
-    int sx_per_token, const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
+    int M, int N, int K) {
     using S = Skinny<MT, WPB, ST>;
     static_assert(ST >= 2 && ST <= 3, "2 or 3 stages");
     __shared__ __attribute__((aligned(1024))) int8_t ring[S::kRing];
@@ -673,7 +679,7 @@ __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
         if (OUT == kOutI32) {
             static_cast<int32_t*>(Y)[o] = a;
         } else {
-            const float f = sx[sx_per_token ? row : 0] * sw[col];
+            const float f = sx[sx_per_token ? row : 0] * sw[sw_per_tensor ? 0 : col];
             const float y = static_cast<float>(a) * f;
             if (OUT == kOutF32)
                 static_cast<float*>(Y)[o] = y;
@@ -685,18 +691,19 @@ __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
 
 template <int MT, int WPB, int ST>
 hipError_t run_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
-                      const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
+                      const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, hipStream_t stream) {
     const dim3 grid((N + 31) / 32), block(64 * WPB);
     const int pt = per_token ? 1 : 0;
+    const int wpt = w_per_tensor ? 1 : 0;
     switch (out) {
         case kOutF32:
-            gemm_skinny_kernel<MT, WPB, ST, kOutF32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            gemm_skinny_kernel<MT, WPB, ST, kOutF32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
             break;
         case kOutBF16:
-            gemm_skinny_kernel<MT, WPB, ST, kOutBF16><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            gemm_skinny_kernel<MT, WPB, ST, kOutBF16><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
             break;
         default:
-            gemm_skinny_kernel<MT, WPB, ST, kOutI32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, y, M, N, K);
+            gemm_skinny_kernel<MT, WPB, ST, kOutI32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
             break;
     }
     return hipGetLastError();
@@ -706,28 +713,28 @@ hipError_t run_skinny(const int8_t* xq, const float* sx, bool per_token, const i
 // and (28672, 8192): four waves per block when there are many channel blocks,
 // eight when there are few; two 32-row X tiles take three stages.
 hipError_t launch_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
-                         const float* sw, int M, int N, int K, void* y, int out, hipStream_t stream) {
+                         const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, hipStream_t stream) {
     const int blocks = (N + 31) / 32;
     if (M <= 32) {
-        if (blocks >= 512) return run_skinny<1, 4, 2>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
-        return run_skinny<1, 8, 2>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
+        if (blocks >= 512) return run_skinny<1, 4, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, stream);
+        return run_skinny<1, 8, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, stream);
     }
-    return run_skinny<2, 4, 3>(xq, sx, per_token, wq, sw, M, N, K, y, out, stream);
+    return run_skinny<2, 4, 3>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
-                       const int8_t* wq, const float* w_scale, int64_t M, int64_t N, int64_t K,
-                       void* y, int out_kind, hipStream_t stream) {
+                       const int8_t* wq, const float* w_scale, bool w_per_tensor, int64_t M,
+                       int64_t N, int64_t K, void* y, int out_kind, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     if (M <= 64) {
         // decode shapes: stream W once, K split over the waves of a block
         if (K % 128 == 0 && N * K < (int64_t(1) << 31)) {
-            return launch_skinny(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
+            return launch_skinny(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, stream);
         }
-        return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
+        return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, stream);
     }
     // ping-pong kernels: K a multiple of the 128-byte stage of the 256x128
     // tile, operand offsets in int32
@@ -740,15 +747,15 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
         const int64_t cost_big = ((t_big + 255) / 256) * 2 * 100;
         const int64_t cost_mid = ((t_mid + 255) / 256) * 105;
         if (cost_big <= cost_mid)
-            return run_pp<256, 256, 2, 4, 64, 3>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y,
+            return run_pp<256, 256, 2, 4, 64, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
                                                  out_kind, stream);
-        return run_pp<256, 128, 4, 2, 128, 3>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y,
+        return run_pp<256, 128, 4, 2, 128, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
                                               out_kind, stream);
     }
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 127) / 128);
     if (big_tiles >= 256)
-        return run<256, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
-    return run<128, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, m, n, k, y, out_kind, stream);
+        return run<256, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, stream);
+    return run<128, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, stream);
 }
 
 }  // namespace sq

@@ -10,13 +10,14 @@
 namespace sq {
 
 enum class Dt : int { F32 = 0, BF16 = 1 };
+enum class ActMode : int { PerToken = 0, Static = 1, DynamicTensor = 2 };
 
 // v rounded up to a whole number of 64-lane waves.
 inline int round_up64(int64_t v) { return static_cast<int>(((v + 63) / 64) * 64); }
 
 // Calibration (offline half).
 hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w, Dt w_dt,
-                            int64_t N, int64_t K, float alpha, const float* gamma,
+                            int64_t N, int64_t K, float alpha, bool w_per_tensor, const float* gamma,
                             const float* beta, float* s, int8_t* wq, float* w_scale,
                             float* act_scale_static, float* gamma_s, float* beta_s,
                             float* x_absmax, float* w_absmax, hipStream_t stream);
@@ -24,12 +25,17 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
 // Activation smoothing + quantization (runtime).
 hipError_t launch_act_quant(const void* x, Dt x_dt, int64_t M, int64_t K, const float* s,
                             const float* gamma_s, const float* beta_s, float eps,
-                            bool static_mode, const float* static_scale, int8_t* xq,
+                            ActMode mode, const float* static_scale, int8_t* xq,
                             float* x_scale, hipStream_t stream);
 
+// step[0] = RN(max(FLOOR, max_i maxima[i]) / 127): the per-tensor step from n
+// non-negative maxima (one block).
+hipError_t launch_tensor_step(const float* maxima, int64_t n, float* step, hipStream_t stream);
+
 // Int8 GEMM with dequantizing epilogue.  out_kind: 0 = f32, 1 = bf16, 2 = i32.
+// w_per_tensor: w_scale[0] is the step of every output channel.
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
-                       const int8_t* wq, const float* w_scale, int64_t M, int64_t N, int64_t K,
-                       void* y, int out_kind, hipStream_t stream);
+                       const int8_t* wq, const float* w_scale, bool w_per_tensor, int64_t M,
+                       int64_t N, int64_t K, void* y, int out_kind, hipStream_t stream);
 
 }  // namespace sq
