@@ -68,6 +68,9 @@ def lib():
         L.orc_gemm_i32.argtypes = [i8p, i8p, i64, i64, i64, vp]
         L.orc_gemm_i32.restype = ci
         L.orc_dequant.argtypes = [vp, f32p, ci, f32p, ci, i64, i64, f32p]
+        L.orc_epilogue.argtypes = [f32p, i64, i64, vp, ci, f32p]
+        L.orc_requant.argtypes = [f32p, i64, i64, vp, cf, i8p]
+        L.orc_requant.restype = ctypes.c_int64
         L.orc_weight_quant_per_tensor.argtypes = [vp, ci, i64, i64, f32p, i8p]
         L.orc_weight_quant_per_tensor.restype = ctypes.c_float
         L.orc_quant_dynamic_per_tensor.argtypes = [f32p, i64, i64, i8p]
@@ -259,6 +262,28 @@ def dequant(acc, x_scale, w_scale, per_token: bool = True,
     return y
 
 
+def epilogue(y, bias=None, relu=False) -> np.ndarray:
+    """Bias (one RN addition) then ReLU (y > 0 ? y : +0) on fp32 outputs."""
+    y = _f32(y)
+    M, N = y.shape
+    b = None if bias is None else _f32(bias)
+    out = np.empty_like(y)
+    lib().orc_epilogue(y.ctypes.data, M, N, None if b is None else b.ctypes.data, int(bool(relu)),
+                       out.ctypes.data)
+    return out
+
+
+def requant(y, next_s, step):
+    """int8 codes of y for the next linear (smoothing s', static step): (codes, n_saturated)."""
+    y = _f32(y)
+    M, N = y.shape
+    ns = None if next_s is None else _f32(next_s)
+    q = np.empty((M, N), np.int8)
+    sat = lib().orc_requant(y.ctypes.data, M, N, None if ns is None else ns.ctypes.data,
+                            float(np.float32(step)), q.ctypes.data)
+    return q, int(sat)
+
+
 def f32_to_bf16(y) -> np.ndarray:
     y = _f32(y)
     out = np.empty(y.shape, np.uint16)
@@ -340,11 +365,18 @@ def smooth_quantize_act(x, s=None, g_s=None, b_s=None, eps=1e-5, static=None, ro
     return q, np.array([static], np.float32), sat
 
 
-def gemm_w8a8(xq, x_scale, wq, w_scale, per_token=True, out="f32", w_per_tensor=False):
+def gemm_w8a8(xq, x_scale, wq, w_scale, per_token=True, out="f32", w_per_tensor=False,
+              bias=None, relu=False, next_s=None, next_scale=None):
+    """Int8 GEMM, dequantization, then the optional fused epilogue; out "i8"
+    requantizes for the next linear (next_s, next_scale)."""
     acc = gemm_i32(xq, wq)
     if out == "i32":
         return acc
     y = dequant(acc, x_scale, w_scale, per_token=per_token, w_per_tensor=w_per_tensor)
+    if bias is not None or relu:
+        y = epilogue(y, bias, relu)
+    if out == "i8":
+        return requant(y, next_s, next_scale)[0]
     if out == "bf16":
         return f32_to_bf16(y)
     return y

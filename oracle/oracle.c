@@ -348,6 +348,43 @@ void orc_dequant(const int32_t* acc, const float* x_scale, int x_per_token,
     }
 }
 
+/* Fused epilogue after the dequantization ([Edge] §二: no separate runtime
+ * operator between this GEMM and the next int8 GEMM; [Teach] §七: fused
+ * quantize / dequantize nodes).  Reading (the pages give no formula): the
+ * bias is one more RN addition, ReLU keeps positive values and maps the rest
+ * to +0:  y1 = bias ? RN(y + b_n) : y;  out = relu ? (y1 > 0 ? y1 : +0) : y1. */
+void orc_epilogue(const float* y, int64_t M, int64_t N, const float* bias, int relu, float* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float v = y[m * N + n];
+            if (bias) v = v + bias[n];
+            if (relu) v = (v > 0.0f) ? v : 0.0f;
+            out[m * N + n] = v;
+        }
+    }
+}
+
+/* Requantize the layer output for the next linear: its smoothing X/s' (the
+ * next layer's input channels are this layer's output channels, [Review]
+ * §5.1 eq. (3)) and its static per-tensor step D ([Review] §2.5):
+ * q = clamp(rne(RN(RN(y / s'_n) / D))); next_s NULL means s' = 1.  Returns
+ * the number of codes that saturated. */
+int64_t orc_requant(const float* y, int64_t M, int64_t N, const float* next_s, float D,
+                    int8_t* q) {
+    int64_t sat = 0;
+#pragma omp parallel for schedule(static) reduction(+ : sat)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float xh = next_s ? y[m * N + n] / next_s[n] : y[m * N + n];
+            float qq = xh / D;
+            if (fabsf(rintf(qq)) > ORC_QMAX) ++sat;
+            q[m * N + n] = quantize_code(qq);
+        }
+    }
+    return sat;
+}
+
 /* bf16 = the fp32 value rounded to 8 significand bits, ties to even
  * (inputs are finite). */
 void orc_f32_to_bf16(const float* y, int64_t n, uint16_t* out) {

@@ -108,6 +108,15 @@ int orc_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64
 void orc_dequant(const int32_t* acc, const float* x_scale, int x_per_token,
                  const float* w_scale, int w_per_tensor, int64_t M, int64_t N, float* y);
 
+/* Epilogue after dequantization: optional bias (one RN addition), optional
+ * ReLU (y > 0 ? y : +0). */
+void orc_epilogue(const float* y, int64_t M, int64_t N, const float* bias, int relu, float* out);
+
+/* int8 codes for the next linear: clamp(rne(RN(RN(y / s'_n) / D))), s' = 1 when
+ * next_s is NULL; returns the saturation count. */
+int64_t orc_requant(const float* y, int64_t M, int64_t N, const float* next_s, float D,
+                    int8_t* q);
+
 /* fp32 -> bf16 bit pattern, round to nearest even. */
 void orc_f32_to_bf16(const float* y, int64_t n, uint16_t* out);
 

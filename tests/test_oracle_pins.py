@@ -490,3 +490,50 @@ def test_dequant_per_tensor_weight_is_broadcast():
     y_t = oracle.dequant(acc, xs, np.array([d], np.float32), per_token=True, w_per_tensor=True)
     y_c = oracle.dequant(acc, xs, np.full(13, d, np.float32), per_token=True)
     assert np.array_equal(y_t.view(np.uint32), y_c.view(np.uint32))
+
+
+# ---- fused epilogue: bias, ReLU, requantization for the next linear ---------------
+
+def test_fused_epilogue_hand_example():
+    g = _golden_kv("fused_epilogue_example.txt")
+    f = lambda k: np.array(g[k], np.float32)
+    out = oracle.epilogue(f("y")[None, :], f("bias"), relu=True)
+    assert np.array_equal(out[0], f("after_relu"))
+    q, sat = oracle.requant(out, f("next_s"), np.float32(g["step"][0]))
+    assert q[0].tolist() == [int(v) for v in g["codes"]]
+    assert sat == int(g["saturated"][0])
+
+
+def test_requant_reduces_to_the_pinned_act_path():
+    """Requantizing fp32 outputs equals the (separately pinned) plain smoothing
+    followed by the static quantizer on the same fp32 tensor -- the fused and
+    the unfused graph give the same codes -- and with s' = 1 it is the static
+    quantizer itself."""
+    rng = np.random.default_rng(5)
+    y = (rng.standard_normal((23, 192)) * 4).astype(np.float32)
+    y[3, 5] = 900.0                                    # saturates
+    ns = rng.uniform(0.05, 20.0, 192).astype(np.float32)
+    D = np.float32(0.031)
+    q, sat = oracle.requant(y, ns, D)
+    xh = oracle.act_smooth(y, ns)
+    q2, sat2 = oracle.quant_static(xh, D)
+    assert np.array_equal(q, q2) and sat == sat2 and sat >= 1
+    q1, _ = oracle.requant(y, None, D)
+    q3, _ = oracle.quant_static(y, D)
+    assert np.array_equal(q1, q3)
+
+
+def test_epilogue_identities_and_relu_sign():
+    """No bias and no ReLU is the identity; ReLU outputs are >= +0 (no -0) and
+    equal the input where it is positive; a zero bias changes nothing."""
+    rng = np.random.default_rng(6)
+    y = (rng.standard_normal((9, 40)) * 3).astype(np.float32)
+    y[0, :4] = [-0.0, 0.0, -1e-30, 1e-30]
+    assert np.array_equal(oracle.epilogue(y).view(np.uint32), y.view(np.uint32))
+    r = oracle.epilogue(y, relu=True)
+    assert np.all(np.signbit(r) == False)              # noqa: E712
+    pos = y > 0
+    assert np.array_equal(r[pos], y[pos]) and np.all(r[~pos] == 0)
+    z = oracle.epilogue(y, np.zeros(40, np.float32))
+    nz = y != 0                                        # -0 + +0 is +0 under RN
+    assert np.array_equal(z[nz].view(np.uint32), y[nz].view(np.uint32))
