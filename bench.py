@@ -115,6 +115,10 @@ def main():
                          "per token (default); O1-O3 = the per-tensor weight settings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--fuse-ffn", action="store_true",
+                    help="opt6.7b: fc1's GEMM epilogue applies ReLU and writes fc2's int8 input "
+                         "codes (fc2's smoothing factor and static step), so fc2 has no "
+                         "activation quantizer call; fc2's GEMM reads a static per-tensor step")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the attainable-ceiling probes (MFMA loop, HBM read and copy)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -166,6 +170,18 @@ def main():
     del xc, w, x
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    names = [L["spec"].name for L in layers]
+    fuse = args.fuse_ffn
+    if fuse and not ("fc1" in names and "fc2" in names and a_mode == "per_token"):
+        print("bench.py: --fuse-ffn needs the opt6.7b workload and the colwise or O1 setting",
+              file=sys.stderr)
+        sys.exit(2)
+    i_fc1, i_fc2 = (names.index("fc1"), names.index("fc2")) if fuse else (-1, -1)
+    if fuse:
+        # fc2's calibration outputs are read by fc1's GEMM: make them valid once
+        L2 = layers[i_fc2]
+        sq.sq_calibrate(L2["xc"], L2["w"], L2["spec"].alpha, out=L2["cal_out"], w_mode=w_mode)
+        torch.cuda.synchronize()
 
     def step(ev=None):
         for i, L in enumerate(layers):
@@ -178,7 +194,9 @@ def main():
                 ev[i][1].record(stream)
             st = cal["static_scale"] if a_mode == "static" else None
             xs = None if a_mode == "static" else L["xs"]
-            if spec.ln:
+            if i == i_fc2:
+                pass  # fc2's codes come from fc1's GEMM epilogue
+            elif spec.ln:
                 _, xs_used = sq.sq_smooth_quantize_act(L["x"], None, cal["ln_gamma_s"],
                                                        cal["ln_beta_s"], 1e-5, a_mode, st,
                                                        xq=L["xq"], x_scale=xs)
@@ -187,8 +205,17 @@ def main():
                                                        static_scale=st, xq=L["xq"], x_scale=xs)
             if ev is not None:
                 ev[i][2].record(stream)
-            sq.sq_gemm_w8a8(L["xq"], xs_used, cal["wq"], cal["w_scale"], a_mode, "bf16",
-                            y=L["y"], w_mode=w_mode)
+            if i == i_fc1:
+                c2 = layers[i_fc2]["cal_out"]
+                sq.sq_gemm_w8a8_ex(L["xq"], xs_used, cal["wq"], cal["w_scale"], a_mode, "i8",
+                                   y=layers[i_fc2]["xq"], w_mode=w_mode, relu=True,
+                                   next_s=c2["s"], next_scale=c2["static_scale"])
+            elif i == i_fc2:
+                sq.sq_gemm_w8a8(L["xq"], cal["static_scale"], cal["wq"], cal["w_scale"], "static",
+                                "bf16", y=L["y"], w_mode=w_mode)
+            else:
+                sq.sq_gemm_w8a8(L["xq"], xs_used, cal["wq"], cal["w_scale"], a_mode, "bf16",
+                                y=L["y"], w_mode=w_mode)
             if ev is not None:
                 ev[i][3].record(stream)
 
@@ -236,6 +263,10 @@ def main():
     for i, L in enumerate(layers):
         spec = L["spec"]
         cb, ab, go, gb = _alg(spec, L["M"])
+        if i == i_fc2:
+            ab = 0  # no activation quantizer call
+        if i == i_fc1:
+            gb += -2 * L["M"] * spec.N + L["M"] * spec.N  # int8 output instead of bf16
         tot_ops += go
         cal_b += cb
         act_b += ab
@@ -245,7 +276,7 @@ def main():
             "calibrate_us": round(t_cal[i] * 1e6, 2),
             "calibrate_GBs": round(cb / t_cal[i] / 1e9, 1),
             "act_quant_us": round(t_act[i] * 1e6, 2),
-            "act_quant_GBs": round(ab / t_act[i] / 1e9, 1),
+            "act_quant_GBs": round(ab / t_act[i] / 1e9, 1) if ab else None,
             "gemm_us": round(t_gemm[i] * 1e6, 2),
             "gemm_TOPS": round(go / t_gemm[i] / 1e12, 1),
             "gemm_GBs_alg": round(gb / t_gemm[i] / 1e9, 1),
@@ -310,6 +341,8 @@ def main():
                    "linears_KN": [[L["spec"].K, L["spec"].N] for L in layers],
                    "alpha": wl.layers[0].alpha, "setting": args.setting, "w_scale": w_mode,
                    "act_scale": a_mode, "y_dtype": "bf16",
+                   "fused_ffn": ("fc1 GEMM epilogue: ReLU + int8 codes for fc2 (fc2's s and static "
+                                 "step); fc2 has no activation quantizer call") if fuse else None,
                    "step": "sq_calibrate + sq_smooth_quantize_act + sq_gemm_w8a8 per linear"},
         "roofline": roof,
         "gemm": {"TOPS": round(gemm_ops / tg / 1e12, 1),

@@ -185,6 +185,11 @@ def ln_params(spec: LayerSpec):
     return gamma, beta
 
 
+def bias(spec: LayerSpec) -> np.ndarray:
+    """Output bias of the linear, N(0, 0.1^2) fp32 [N] (seed base + 4)."""
+    return (_rng(spec.seed_base + 4).standard_normal(spec.N) * 0.1).astype(np.float32)
+
+
 def _model_layernorm_f32(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray,
                          eps: float = 1e-5) -> np.ndarray:
     """The model's own (unsmoothed) LayerNorm in fp32 numpy.  Used only to

@@ -52,6 +52,10 @@
  *   acc  = sum_k xq[t,k] * wq[n,k]   (exact int32)
  *   y    = RN(RN_f32(acc) * RN(dx_t * dw_n));  bf16 output = y rounded to
  *          bf16 (nearest even).
+ *   fused epilogue (sq_gemm_w8a8_ex):  y1 = bias ? RN(y + b_n) : y;
+ *          y2 = relu ? (y1 > 0 ? y1 : +0) : y1;  fp32 / bf16 output = y2;
+ *          int8 output = clamp(rne(RN(RN(y2 / s'_n) / D))) with the next
+ *          linear's smoothing factor s' (1 when absent) and static step D.
  */
 #ifndef SQ_H
 #define SQ_H
@@ -178,6 +182,42 @@ sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_mode x_mod
                        const int8_t* wq, const float* w_scale, sq_weight_mode w_mode,
                        int64_t M, int64_t N, int64_t K,
                        void* y, sq_dtype y_dt, sq_stream_t stream);
+
+/*
+ * Fused epilogue of sq_gemm_w8a8_ex.  [Edge] §二 (no separate floating-point
+ * operator between one int8 GEMM and the next: the smoothing of the next layer
+ * is fused, the graph runs quantize -> int8 GEMM -> dequantized output);
+ * [Teach] §七 (the speed-up relies on fused quantize / dequantize nodes).
+ * Bias and ReLU are the linear's own epilogue (the pages give no formula; one
+ * RN addition, and ReLU maps non-positive values to +0).
+ */
+typedef struct sq_epilogue {
+    const float* bias;       /* [N] fp32 added after the dequantization, or NULL */
+    const float* next_s;     /* SQ_I8 output only: [N] smoothing factor s' of the next
+                                linear (whose input channels are these outputs), or
+                                NULL for s' = 1 */
+    const float* next_scale; /* SQ_I8 output only (required): [1] device, the next
+                                linear's static per-tensor step D */
+    int relu;                /* nonzero: ReLU after the bias */
+} sq_epilogue;
+
+/*
+ * sq_gemm_w8a8_ex -- sq_gemm_w8a8 with a fused epilogue.
+ *   epi  NULL: exactly sq_gemm_w8a8.
+ *   y_dt SQ_F32 / SQ_BF16: y2 of the contract above.
+ *        SQ_I8: int8 codes [M, N] for the next linear (static per-tensor
+ *        input step), written instead of the fp32 / bf16 activation -- the
+ *        next layer's sq_smooth_quantize_act is fused away.  Equals, bit for
+ *        bit, sq_smooth_quantize_act(SQ_STATIC_PER_TENSOR, s = next_s) applied
+ *        to the SQ_F32 output with the same epilogue.
+ *        SQ_I32: raw accumulators; epi must then be NULL or empty.
+ * Errors: SQ_ERR_BAD_MODE for next_s with a non-int8 output or an epilogue
+ * with int32 output; SQ_ERR_NULL_ARG for int8 output without next_scale.
+ */
+sq_status sq_gemm_w8a8_ex(const int8_t* xq, const float* x_scale, sq_act_mode x_mode,
+                          const int8_t* wq, const float* w_scale, sq_weight_mode w_mode,
+                          int64_t M, int64_t N, int64_t K, const sq_epilogue* epi,
+                          void* y, sq_dtype y_dt, sq_stream_t stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* sq_status_string(sq_status status);

@@ -173,3 +173,29 @@ def test_probe_library_exports_and_validates():
     assert L.sqp_read(MIS, 64, 4, P, None) == 1           # misaligned
     assert L.sqp_copy(P, MIS, 64, 4, None) == 1
     assert L.sqp_copy(P, P + 64, 0, 4, None) == 1
+
+
+def _gemm_ex(epi, ydt=0, **kw):
+    a = dict(M=4, N=4, K=64, xq=P, xs=P, mode=0, wq=P, ws=P, wmode=0, y=P)
+    a.update(kw)
+    e = None if epi is None else sq.SqEpilogue(*epi)
+    return sq.lib().sq_gemm_w8a8_ex(a["xq"], a["xs"], a["mode"], a["wq"], a["ws"], a["wmode"],
+                                    a["M"], a["N"], a["K"], e, a["y"], ydt, None)
+
+
+def test_gemm_ex_validation():
+    """The fused epilogue: int8 output needs the next layer's step; next_s only
+    with int8 output; raw int32 output takes no epilogue; pointers aligned."""
+    assert _gemm_ex((None, None, None, 0), ydt=2) == 1          # i8 without next_scale
+    assert _gemm_ex((None, P, None, 0), ydt=2) == 1
+    assert _gemm_ex((None, P, P, 0), ydt=1) == 7                # next_s with bf16 output
+    assert _gemm_ex((None, None, P, 0), ydt=0) == 7             # next_scale with f32 output
+    assert _gemm_ex((P, None, None, 0), ydt=3) == 7             # bias with int32 output
+    assert _gemm_ex((None, None, None, 1), ydt=3) == 7          # relu with int32 output
+    assert _gemm_ex((MIS, None, None, 0), ydt=0) == 5
+    assert _gemm_ex((None, MIS, P, 0), ydt=2) == 5
+    assert _gemm_ex(None, ydt=9) == 3
+    assert _gemm_ex(None, ydt=0, K=96) == 2
+    assert _gemm_ex((P, None, None, 1), ydt=0, M=0, xq=None, y=None) == 0
+    # the plain entry point has no int8 output
+    assert _gemm(ydt=2) == 3

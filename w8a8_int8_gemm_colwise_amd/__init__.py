@@ -40,8 +40,14 @@ SETTINGS = {
     "O2": ("per_tensor", "dynamic_per_tensor"),
     "O3": ("per_tensor", "static"),
 }
-EXPORTED = ("sq_calibrate", "sq_smooth_quantize_act", "sq_gemm_w8a8", "sq_status_string",
-            "sq_abi_version")
+EXPORTED = ("sq_calibrate", "sq_smooth_quantize_act", "sq_gemm_w8a8", "sq_gemm_w8a8_ex",
+            "sq_status_string", "sq_abi_version")
+
+
+class SqEpilogue(ctypes.Structure):
+    """struct sq_epilogue of sq.h (fused epilogue of sq_gemm_w8a8_ex)."""
+    _fields_ = [("bias", ctypes.c_void_p), ("next_s", ctypes.c_void_p),
+                ("next_scale", ctypes.c_void_p), ("relu", ctypes.c_int)]
 
 _lib = None
 
@@ -68,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.sq_smooth_quantize_act.argtypes = [vp, ci, i64, i64, vp, vp, vp, cf, ci, vp, vp, vp, vp]
     L.sq_gemm_w8a8.restype = ci
     L.sq_gemm_w8a8.argtypes = [vp, vp, ci, vp, vp, ci, i64, i64, i64, vp, ci, vp]
+    L.sq_gemm_w8a8_ex.restype = ci
+    L.sq_gemm_w8a8_ex.argtypes = [vp, vp, ci, vp, vp, ci, i64, i64, i64,
+                                  ctypes.POINTER(SqEpilogue), vp, ci, vp]
     L.sq_status_string.restype = ctypes.c_char_p
     L.sq_status_string.argtypes = [ci]
     L.sq_abi_version.restype = ci
@@ -181,7 +190,7 @@ def sq_smooth_quantize_act(x: torch.Tensor, s: torch.Tensor | None = None,
 
 
 _OUT = {"f32": (SQ_F32, torch.float32), "bf16": (SQ_BF16, torch.bfloat16),
-        "i32": (SQ_I32, torch.int32)}
+        "i32": (SQ_I32, torch.int32), "i8": (SQ_I8, torch.int8)}
 
 
 def sq_gemm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor,
@@ -200,4 +209,29 @@ def sq_gemm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tenso
         y = torch.empty((M, N), dtype=tdt, device=xq.device)
     _check(lib().sq_gemm_w8a8(_ptr(xq), _ptr(x_scale), _mode(mode), _ptr(wq), _ptr(w_scale),
                               _wmode(w_mode), M, N, K, _ptr(y), code, _stream(xq.device)))
+    return y
+
+
+def sq_gemm_w8a8_ex(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor,
+                    w_scale: torch.Tensor | None, mode="per_token", out_dtype: str = "bf16",
+                    y: torch.Tensor | None = None, w_mode="per_channel",
+                    bias: torch.Tensor | None = None, relu: bool = False,
+                    next_s: torch.Tensor | None = None,
+                    next_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """Int8 GEMM with the fused epilogue: dequantize, + bias, ReLU, then fp32 /
+    bf16 output, or (out_dtype "i8") the next linear's int8 codes for its
+    smoothing factor next_s and static step next_scale [1]."""
+    _dev2d(xq, "xq")
+    _dev2d(wq, "wq")
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K != K2:
+        raise ValueError("xq and wq disagree on K")
+    code, tdt = _OUT[out_dtype]
+    if y is None:
+        y = torch.empty((M, N), dtype=tdt, device=xq.device)
+    epi = SqEpilogue(_ptr(bias), _ptr(next_s), _ptr(next_scale), int(bool(relu)))
+    _check(lib().sq_gemm_w8a8_ex(_ptr(xq), _ptr(x_scale), _mode(mode), _ptr(wq), _ptr(w_scale),
+                                 _wmode(w_mode), M, N, K, ctypes.byref(epi), _ptr(y), code,
+                                 _stream(xq.device)))
     return y

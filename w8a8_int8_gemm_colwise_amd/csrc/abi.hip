@@ -82,27 +82,48 @@ sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
-sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_mode x_mode,
-                       const int8_t* wq, const float* w_scale, sq_weight_mode w_mode, int64_t M,
-                       int64_t N, int64_t K, void* y, sq_dtype y_dt, sq_stream_t stream) {
+sq_status sq_gemm_w8a8_ex(const int8_t* xq, const float* x_scale, sq_act_mode x_mode,
+                          const int8_t* wq, const float* w_scale, sq_weight_mode w_mode,
+                          int64_t M, int64_t N, int64_t K, const sq_epilogue* epi, void* y,
+                          sq_dtype y_dt, sq_stream_t stream) {
     if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return SQ_ERR_BAD_SHAPE;
     if (M * N > (int64_t(1) << 40)) return SQ_ERR_BAD_SHAPE;
-    if (y_dt != SQ_F32 && y_dt != SQ_BF16 && y_dt != SQ_I32) return SQ_ERR_BAD_DTYPE;
+    if (y_dt != SQ_F32 && y_dt != SQ_BF16 && y_dt != SQ_I32 && y_dt != SQ_I8)
+        return SQ_ERR_BAD_DTYPE;
     if (x_mode != SQ_PER_TOKEN && x_mode != SQ_STATIC_PER_TENSOR &&
         x_mode != SQ_DYNAMIC_PER_TENSOR)
         return SQ_ERR_BAD_MODE;
     if (w_mode != SQ_W_PER_CHANNEL && w_mode != SQ_W_PER_TENSOR) return SQ_ERR_BAD_MODE;
+    sq::Epi e;
+    if (epi) {
+        e.bias = epi->bias;
+        e.next_s = epi->next_s;
+        e.next_step = epi->next_scale;
+        e.relu = epi->relu != 0;
+    }
+    const bool any = e.bias || e.next_s || e.next_step || e.relu;
+    if (y_dt == SQ_I32 && any) return SQ_ERR_BAD_MODE;
+    if (y_dt != SQ_I8 && (e.next_s || e.next_step)) return SQ_ERR_BAD_MODE;
+    if (y_dt == SQ_I8 && !e.next_step) return SQ_ERR_NULL_ARG;
     if (M > 0 && N > 0) {
         if (!xq || !wq || !y) return SQ_ERR_NULL_ARG;
         if (y_dt != SQ_I32 && (!x_scale || !w_scale)) return SQ_ERR_NULL_ARG;
     }
-    const void* ptrs[] = {xq, x_scale, wq, w_scale, y};
+    const void* ptrs[] = {xq, x_scale, wq, w_scale, y, e.bias, e.next_s, e.next_step};
     for (const void* p : ptrs)
         if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
-    const int out = (y_dt == SQ_F32) ? 0 : (y_dt == SQ_BF16) ? 1 : 2;
+    const int out = (y_dt == SQ_F32) ? 0 : (y_dt == SQ_BF16) ? 1 : (y_dt == SQ_I32) ? 2 : 3;
     return from_hip(sq::launch_gemm(xq, x_scale, x_mode == SQ_PER_TOKEN, wq, w_scale,
-                                    w_mode == SQ_W_PER_TENSOR, M, N, K, y, out,
+                                    w_mode == SQ_W_PER_TENSOR, M, N, K, y, out, e,
                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_mode x_mode,
+                       const int8_t* wq, const float* w_scale, sq_weight_mode w_mode, int64_t M,
+                       int64_t N, int64_t K, void* y, sq_dtype y_dt, sq_stream_t stream) {
+    if (y_dt == SQ_I8) return SQ_ERR_BAD_DTYPE;  // int8 output needs the fused epilogue
+    return sq_gemm_w8a8_ex(xq, x_scale, x_mode, wq, w_scale, w_mode, M, N, K, nullptr, y, y_dt,
+                           stream);
 }
 
 const char* sq_status_string(sq_status status) {

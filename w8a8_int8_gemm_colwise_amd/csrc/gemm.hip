@@ -56,7 +56,49 @@ __device__ __forceinline__ int lds_off_k(int row, int chunk) {
     return row * BK + ((chunk ^ swz_k<BK>(row)) << 4);
 }
 
-enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2 };
+enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2, kOutI8 = 3 };
+
+// Fused epilogue on a dequantized value y (see Epi): bias, then ReLU to +0.
+__device__ __forceinline__ float bias_relu(float y, bool has_bias, float b, int relu) {
+    if (has_bias) y = y + b;
+    if (relu) y = (y > 0.0f) ? y : 0.0f;
+    return y;
+}
+
+// int8 code of y for the next linear: RN(y / s') (skipped when s' = 1), then
+// the static quantizer with step D: the dividend is limited to +-128 D (an
+// exact power-of-two scaling that leaves every code unchanged), then
+// clamp(rne(RN(. / D))).  rs = RN(1 / s'), rD = RN(1 / D) for the exact division.
+__device__ __forceinline__ int requant_code(float y, bool has_s, float sv, float rs, float D,
+                                            float rD) {
+    float xh = has_s ? div_rn(y, sv, rs) : y;
+    const float lim = 128.0f * D;
+    xh = fminf(fmaxf(xh, -lim), lim);
+    return code_of(div_rn(xh, D, rD));
+}
+
+// One output element of the plain epilogues (register-staged and skinny
+// kernels): dequantize, fuse, store.  o = row * N + col.
+template <int OUT>
+__device__ __forceinline__ void store_elem(void* __restrict__ Y, int64_t o, int a, float dx,
+                                           float dw, const Epi& e, int col, float D, float rD) {
+    if (OUT == kOutI32) {
+        static_cast<int32_t*>(Y)[o] = a;
+        return;
+    }
+    const float f = dx * dw;
+    float y = static_cast<float>(a) * f;
+    y = bias_relu(y, e.bias != nullptr, e.bias ? e.bias[col] : 0.0f, e.relu);
+    if (OUT == kOutF32) {
+        static_cast<float*>(Y)[o] = y;
+    } else if (OUT == kOutBF16) {
+        static_cast<__bf16*>(Y)[o] = static_cast<__bf16>(y);
+    } else {
+        const bool hs = e.next_s != nullptr;
+        const float sv = hs ? e.next_s[col] : 1.0f;
+        static_cast<int8_t*>(Y)[o] = static_cast<int8_t>(requant_code(y, hs, sv, 1.0f / sv, D, rD));
+    }
+}
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 struct Tile {
@@ -97,9 +139,11 @@ template <int OUT, int TM, int TN>
 __device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int row0, int col0, int lane,
                                            const float* __restrict__ sx, int sx_per_token,
                                            const float* __restrict__ sw, int sw_per_tensor,
-                                           void* __restrict__ Y, int M, int N) {
+                                           void* __restrict__ Y, int M, int N, const Epi& e) {
     const int frow = lane & 31;
     const int fhalf = lane >> 5;
+    const float D = (OUT == kOutI8) ? *e.next_step : 1.0f;
+    const float rD = 1.0f / D;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -115,16 +159,8 @@ __device__ __forceinline__ void store_tile(const v16i (&acc)[TM][TN], int row0, 
                     if (col >= N) continue;
                     const int a = acc[i][j][4 * g + r];
                     const int64_t o = static_cast<int64_t>(row) * N + col;
-                    if (OUT == kOutI32) {
-                        static_cast<int32_t*>(Y)[o] = a;
-                    } else {
-                        const float f = dx * sw[sw_per_tensor ? 0 : col];
-                        const float y = static_cast<float>(a) * f;
-                        if (OUT == kOutF32)
-                            static_cast<float*>(Y)[o] = y;
-                        else
-                            static_cast<__bf16*>(Y)[o] = static_cast<__bf16>(y);
-                    }
+                    const float dw = (OUT == kOutI32) ? 0.0f : sw[sw_per_tensor ? 0 : col];
+                    store_elem<OUT>(Y, o, a, dx, dw, e, col, D, rD);
                 }
             }
         }
@@ -135,7 +171,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
-    int M, int N, int K) {
+    int M, int N, int K, Epi epi) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     static_assert(T::LA * T::kThreads == BM * kChunksPerRow, "A tile divides over threads");
     static_assert(T::LB * T::kThreads == BN * kChunksPerRow, "B tile divides over threads");
@@ -235,12 +271,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     }
 
     store_tile<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + wn * T::WN, lane, sx, sx_per_token,
-                                  sw, sw_per_tensor, Y, M, N);
+                                  sw, sw_per_tensor, Y, M, N, epi);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
-               const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, hipStream_t stream) {
+               const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, const Epi& epi,
+                    hipStream_t stream) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(tiles), block(T::kThreads);
@@ -249,15 +286,19 @@ hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* 
     switch (out) {
         case kOutF32:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutF32><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, wpt, y, M, N, K);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
             break;
         case kOutBF16:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutBF16><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, wpt, y, M, N, K);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+            break;
+        case kOutI8:
+            gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutI8><<<grid, block, 0, stream>>>(
+                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
             break;
         default:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutI32><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, wpt, y, M, N, K);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
             break;
     }
     return hipGetLastError();
@@ -272,17 +313,27 @@ hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* 
 // keeps a write instruction free of bank conflicts) and leave as whole
 // 16-byte chunks, several lanes per row, so each global store instruction
 // covers complete 128-byte row segments.  sxs / sws: LDS copies of the scales
-// of the wave tile's rows and columns.  The dequantization is the library's
-// fixed order: f = s_x * s_w, then y = float(acc) * f, rounded once to the
-// output type.
+// of the wave tile's rows and columns; bcs / scs / rcs: LDS copies of the
+// columns' bias, next-layer smoothing factor s' and RN(1/s') (fused epilogue).
+// The dequantization is the library's fixed order: f = s_x * s_w, then
+// y = float(acc) * f, then bias and ReLU, then the output type (bf16 rounding,
+// or the next linear's int8 code).
+template <int OUT>
+constexpr int out_bytes() { return OUT == kOutBF16 ? 2 : OUT == kOutI8 ? 1 : 4; }
+
+template <int OUT, int TN>
+constexpr int epi_pitch() { return TN * 32 * out_bytes<OUT>() + (out_bytes<OUT>() == 4 ? 16 : 8); }
+
 template <int OUT, int TM, int TN>
 __device__ __forceinline__ void store_tile_t(const v16i (&acc)[TM][TN], int row0, int col0,
                                              int lane, const float* sxs, const float* sws,
+                                             const float* bcs, const float* scs,
+                                             const float* rcs, const Epi& e, float D, float rD,
                                              void* __restrict__ Y, int M, int N,
                                              int8_t* scratch) {
-    constexpr int ES = (OUT == kOutBF16) ? 2 : 4;  // output element bytes
+    constexpr int ES = out_bytes<OUT>();            // output element bytes
     constexpr int SEG = TN * 32 * ES;              // bytes of one row of the wave tile
-    constexpr int PITCH = SEG + (ES == 2 ? 8 : 16);
+    constexpr int PITCH = epi_pitch<OUT, TN>();
     constexpr int CPR = SEG / 16;                  // 16-byte chunks per row
     constexpr int EPC = 16 / ES;                   // elements per chunk
     static_assert((32 * CPR) % 64 == 0, "whole chunks per lane");
@@ -305,19 +356,37 @@ __device__ __forceinline__ void store_tile_t(const v16i (&acc)[TM][TN], int row0
                 } else {
                     const float4 w = *reinterpret_cast<const float4*>(sws + c);
                     const float dw[4] = {w.x, w.y, w.z, w.w};
+                    const bool hb = e.bias != nullptr;
+                    float4 bv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    if (hb) bv = *reinterpret_cast<const float4*>(bcs + c);
+                    const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
                     float y[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float f = dx * dw[e];
-                        y[e] = static_cast<float>(acc[i][j][4 * g + e]) * f;
+                    for (int t = 0; t < 4; ++t) {
+                        const float f = dx * dw[t];
+                        y[t] = bias_relu(static_cast<float>(acc[i][j][4 * g + t]) * f, hb, bb[t],
+                                         e.relu);
                     }
                     if (OUT == kOutF32) {
                         *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
-                    } else {
+                    } else if (OUT == kOutBF16) {
                         typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
                         bf4 b;
-                        for (int e = 0; e < 4; ++e) b[e] = static_cast<__bf16>(y[e]);
+                        for (int t = 0; t < 4; ++t) b[t] = static_cast<__bf16>(y[t]);
                         *reinterpret_cast<bf4*>(dst) = b;
+                    } else {
+                        const bool hs = e.next_s != nullptr;
+                        const float4 sv = *reinterpret_cast<const float4*>(scs + c);
+                        const float4 rv = *reinterpret_cast<const float4*>(rcs + c);
+                        const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
+                        const float rr[4] = {rv.x, rv.y, rv.z, rv.w};
+                        uint32_t packed = 0;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int q = requant_code(y[t], hs, ss[t], rr[t], D, rD);
+                            packed |= (static_cast<uint32_t>(q) & 0xffu) << (8 * t);
+                        }
+                        *reinterpret_cast<uint32_t*>(dst) = packed;
                     }
                 }
             }
@@ -408,7 +477,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OUT>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
-    int M, int N, int K) {
+    int M, int N, int K, Epi epi) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     static_assert(WAVES_M * WAVES_N == 8, "two groups of four waves");
     constexpr int kRows = BM + BN;
@@ -420,11 +489,12 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     static_assert(IPW * 8 * kRowsPerXfer == kRows, "stage divides over the waves");
     static_assert(BM % kRowsPerXfer == 0, "a transfer never straddles A and B");
     static_assert(STAGES >= 3, "a refill needs two phases of slack");
-    constexpr int kEpiPitch = T::TN * 32 * (OUT == kOutBF16 ? 2 : 4) + (OUT == kOutBF16 ? 8 : 16);
+    constexpr int kEpiPitch = epi_pitch<OUT, T::TN>();
     static_assert(8 * 32 * kEpiPitch <= STAGES * kStageBytes, "epilogue scratch fits");
     static_assert(BM + BN <= 512, "one scale per thread");
     __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * kStageBytes];
     __shared__ __attribute__((aligned(16))) float scales[BM + BN];  // row scales, then column scales
+    __shared__ __attribute__((aligned(16))) float epi_cols[3 * BN];  // bias, s', RN(1/s') per column
 
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
@@ -485,15 +555,27 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     // the tile's scales: loaded before the first transfers are issued, stored
     // to LDS after stage 0 has landed (the store waits for every load in
     // flight, stages 1.. included, once per tile)
-    float scale = 0.0f;
+    float scale = 0.0f, cb = 0.0f, cs = 1.0f;
     const int st = threadIdx.x;
     if (OUT != kOutI32 && st < BM + BN)
         scale = st < BM ? sx[sx_per_token ? min(m0 + st, M - 1) : 0]
                         : sw[sw_per_tensor ? 0 : min(n0 + st - BM, N - 1)];
+    if (OUT != kOutI32 && st < BN) {
+        const int col = min(n0 + st, N - 1);
+        if (epi.bias) cb = epi.bias[col];
+        if (OUT == kOutI8 && epi.next_s) cs = epi.next_s[col];
+    }
+    const float D = (OUT == kOutI8) ? *epi.next_step : 1.0f;
+    const float rD = 1.0f / D;
     compiler_fence();
     for (int t = 0; t < STAGES - 1 && t < KT; ++t) issue(t);
     wait_stage(0);
     if (OUT != kOutI32 && st < BM + BN) scales[st] = scale;
+    if (OUT != kOutI32 && st < BN) {
+        epi_cols[st] = cb;
+        epi_cols[BN + st] = cs;
+        epi_cols[2 * BN + st] = 1.0f / cs;
+    }
     bar();
     if (group == 1) bar();
     for (int t = 0; t < KT; ++t) {
@@ -531,14 +613,17 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     if (group == 0) bar();
 
     __syncthreads();
-    store_tile_t<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + wn * T::WN, lane,
-                                    scales + wm * T::WM, scales + BM + wn * T::WN, Y, M, N,
+    const int cw = wn * T::WN;
+    store_tile_t<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + cw, lane, scales + wm * T::WM,
+                                    scales + BM + cw, epi_cols + cw, epi_cols + BN + cw,
+                                    epi_cols + 2 * BN + cw, epi, D, rD, Y, M, N,
                                     lds + wave * (32 * kEpiPitch));
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
 hipError_t run_pp(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
-                  const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, hipStream_t stream) {
+                  const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, const Epi& epi,
+                    hipStream_t stream) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid(tiles), block(512);
     const int pt = per_token ? 1 : 0;
@@ -546,15 +631,19 @@ hipError_t run_pp(const int8_t* xq, const float* sx, bool per_token, const int8_
     switch (out) {
         case kOutF32:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutF32>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
             break;
         case kOutBF16:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutBF16>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+            break;
+        case kOutI8:
+            gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutI8>
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
             break;
         default:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutI32>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
             break;
     }
     return hipGetLastError();
@@ -599,7 +688,7 @@ template <int MT, int WPB, int ST, int OUT>
 __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
-    int M, int N, int K) {
+    int M, int N, int K, Epi epi) {
     using S = Skinny<MT, WPB, ST>;
     static_assert(ST >= 2 && ST <= 3, "2 or 3 stages");
     __shared__ __attribute__((aligned(1024))) int8_t ring[S::kRing];
@@ -609,6 +698,8 @@ __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
     const int n0 = blockIdx.x * 32;
     const int frow = lane & 31;
     const int half = lane >> 5;
+    const float D = (OUT == kOutI8) ? *epi.next_step : 1.0f;
+    const float rD = 1.0f / D;
 
     for (int i = threadIdx.x; i < MT * 32 * 32; i += 64 * WPB) red[i] = 0;
 
@@ -676,34 +767,31 @@ __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
         if (row >= M || col >= N) continue;
         const int a = red[i];
         const int64_t o = static_cast<int64_t>(row) * N + col;
-        if (OUT == kOutI32) {
-            static_cast<int32_t*>(Y)[o] = a;
-        } else {
-            const float f = sx[sx_per_token ? row : 0] * sw[sw_per_tensor ? 0 : col];
-            const float y = static_cast<float>(a) * f;
-            if (OUT == kOutF32)
-                static_cast<float*>(Y)[o] = y;
-            else
-                static_cast<__bf16*>(Y)[o] = static_cast<__bf16>(y);
-        }
+        const float dx = (OUT == kOutI32) ? 0.0f : sx[sx_per_token ? row : 0];
+        const float dw = (OUT == kOutI32) ? 0.0f : sw[sw_per_tensor ? 0 : col];
+        store_elem<OUT>(Y, o, a, dx, dw, epi, col, D, rD);
     }
 }
 
 template <int MT, int WPB, int ST>
 hipError_t run_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
-                      const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, hipStream_t stream) {
+                      const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, const Epi& epi,
+                    hipStream_t stream) {
     const dim3 grid((N + 31) / 32), block(64 * WPB);
     const int pt = per_token ? 1 : 0;
     const int wpt = w_per_tensor ? 1 : 0;
     switch (out) {
         case kOutF32:
-            gemm_skinny_kernel<MT, WPB, ST, kOutF32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
+            gemm_skinny_kernel<MT, WPB, ST, kOutF32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
             break;
         case kOutBF16:
-            gemm_skinny_kernel<MT, WPB, ST, kOutBF16><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
+            gemm_skinny_kernel<MT, WPB, ST, kOutBF16><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+            break;
+        case kOutI8:
+            gemm_skinny_kernel<MT, WPB, ST, kOutI8><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
             break;
         default:
-            gemm_skinny_kernel<MT, WPB, ST, kOutI32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K);
+            gemm_skinny_kernel<MT, WPB, ST, kOutI32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
             break;
     }
     return hipGetLastError();
@@ -713,28 +801,30 @@ hipError_t run_skinny(const int8_t* xq, const float* sx, bool per_token, const i
 // and (28672, 8192): four waves per block when there are many channel blocks,
 // eight when there are few; two 32-row X tiles take three stages.
 hipError_t launch_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
-                         const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, hipStream_t stream) {
+                         const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, const Epi& epi,
+                    hipStream_t stream) {
     const int blocks = (N + 31) / 32;
     if (M <= 32) {
-        if (blocks >= 512) return run_skinny<1, 4, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, stream);
-        return run_skinny<1, 8, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, stream);
+        if (blocks >= 512) return run_skinny<1, 4, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, epi, stream);
+        return run_skinny<1, 8, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, epi, stream);
     }
-    return run_skinny<2, 4, 3>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, stream);
+    return run_skinny<2, 4, 3>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, epi, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
                        const int8_t* wq, const float* w_scale, bool w_per_tensor, int64_t M,
-                       int64_t N, int64_t K, void* y, int out_kind, hipStream_t stream) {
+                       int64_t N, int64_t K, void* y, int out_kind, const Epi& epi,
+                       hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     if (M <= 64) {
         // decode shapes: stream W once, K split over the waves of a block
         if (K % 128 == 0 && N * K < (int64_t(1) << 31)) {
-            return launch_skinny(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, stream);
+            return launch_skinny(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, stream);
         }
-        return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, stream);
+        return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, stream);
     }
     // ping-pong kernels: K a multiple of the 128-byte stage of the 256x128
     // tile, operand offsets in int32
@@ -748,14 +838,14 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
         const int64_t cost_mid = ((t_mid + 255) / 256) * 105;
         if (cost_big <= cost_mid)
             return run_pp<256, 256, 2, 4, 64, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
-                                                 out_kind, stream);
+                                                 out_kind, epi, stream);
         return run_pp<256, 128, 4, 2, 128, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
-                                              out_kind, stream);
+                                              out_kind, epi, stream);
     }
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 127) / 128);
     if (big_tiles >= 256)
-        return run<256, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, stream);
-    return run<128, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, stream);
+        return run<256, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, stream);
+    return run<128, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, stream);
 }
 
 }  // namespace sq

@@ -32,10 +32,22 @@ hipError_t launch_act_quant(const void* x, Dt x_dt, int64_t M, int64_t K, const 
 // non-negative maxima (one block).
 hipError_t launch_tensor_step(const float* maxima, int64_t n, float* step, hipStream_t stream);
 
-// Int8 GEMM with dequantizing epilogue.  out_kind: 0 = f32, 1 = bf16, 2 = i32.
+// Fused GEMM epilogue after the dequantization: bias (one RN addition), ReLU
+// (y > 0 ? y : +0), and for int8 output the next linear's smoothing division
+// and static step, clamp(rne(RN(RN(y / s'_n) / D))).
+struct Epi {
+    const float* bias = nullptr;       // [N] or null
+    const float* next_s = nullptr;     // [N] or null (s' = 1); int8 output only
+    const float* next_step = nullptr;  // [1] device, D; required for int8 output
+    int relu = 0;
+};
+
+// Int8 GEMM with dequantizing epilogue.  out_kind: 0 = f32, 1 = bf16, 2 = i32
+// (raw accumulators, epilogue unused), 3 = i8 (requantized for the next linear).
 // w_per_tensor: w_scale[0] is the step of every output channel.
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
                        const int8_t* wq, const float* w_scale, bool w_per_tensor, int64_t M,
-                       int64_t N, int64_t K, void* y, int out_kind, hipStream_t stream);
+                       int64_t N, int64_t K, void* y, int out_kind, const Epi& epi,
+                       hipStream_t stream);
 
 }  // namespace sq
