@@ -380,3 +380,13 @@ def gemm_w8a8(xq, x_scale, wq, w_scale, per_token=True, out="f32", w_per_tensor=
     if out == "bf16":
         return f32_to_bf16(y)
     return y
+
+
+def bmm_w8a8(xq, x_scale, wq, w_scale, per_token=True, w_per_tensor=False, out="f32"):
+    """Batched int8 GEMM ([Review] §5.6, Fig. 6: the batched matrix products of
+    attention run in int8 like the linear layers): entry b is gemm_w8a8 of
+    xq[b] [M, K] with wq[b] [N, K] and the b-th scale vectors."""
+    B = xq.shape[0]
+    outs = [gemm_w8a8(xq[b], x_scale[b], wq[b], w_scale[b], per_token=per_token, out=out,
+                      w_per_tensor=w_per_tensor) for b in range(B)]
+    return np.stack(outs)

@@ -537,3 +537,30 @@ def test_epilogue_identities_and_relu_sign():
     z = oracle.epilogue(y, np.zeros(40, np.float32))
     nz = y != 0                                        # -0 + +0 is +0 under RN
     assert np.array_equal(z[nz].view(np.uint32), y[nz].view(np.uint32))
+
+
+# ---- int8 attention products ([Review] §5.6, Fig. 6) ------------------------------
+
+def test_int8_attention_scores_within_quantizer_bound():
+    """S = Q K^T with both operands quantized per token (no smoothing): every
+    dequantized score lies within the quantizer's error bound of the fp64
+    product, sum_k(|q_k| dk/2 + |k_k| dq/2 + dq dk/4) plus fp32 rounding, and
+    the batched oracle is the per-head GEMM with the head's scales."""
+    rng = np.random.default_rng(11)
+    H, S, d = 3, 37, 64
+    q = rng.standard_normal((H, S, d)).astype(np.float32)
+    k = rng.standard_normal((H, S, d)).astype(np.float32)
+    q[1, 4, 9] = 30.0                                  # a head with an outlier query
+    ones = np.ones(d, np.float32)
+    qq, qs = zip(*[oracle.quant_per_token(oracle.act_smooth(q[h], ones)) for h in range(H)])
+    kq, ks = zip(*[oracle.quant_per_token(oracle.act_smooth(k[h], ones)) for h in range(H)])
+    qq, qs, kq, ks = map(np.stack, (qq, qs, kq, ks))
+    s = oracle.bmm_w8a8(qq, qs, kq, ks)
+    for h in range(H):
+        exact = q[h].astype(np.float64) @ k[h].astype(np.float64).T
+        dq, dk = qs[h].astype(np.float64)[:, None], ks[h].astype(np.float64)[None, :]
+        bound = (np.abs(q[h]).astype(np.float64) @ np.ones((d, 1))) * dk / 2 \
+            + dq / 2 * (np.ones((1, d)) @ np.abs(k[h]).astype(np.float64).T) + d * dq * dk / 4
+        err = np.abs(s[h].astype(np.float64) - exact)
+        assert np.all(err <= bound * (1 + 1e-6) + np.abs(exact) * 2.0 ** -22)
+        assert np.array_equal(s[h], oracle.gemm_w8a8(qq[h], qs[h], kq[h], ks[h]))
