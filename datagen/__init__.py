@@ -263,3 +263,32 @@ def random_layer(M: int, N: int, K: int, seed: int, x_dtype: str = "bf16",
                      x_dtype=x_dtype, w_std=0.02, w_dtype=w_dtype, outlier_frac=None,
                      n_outliers_fixed=min(n_outliers, K), outlier_sign="entry", alpha=alpha,
                      mode=mode, ln=ln, seed_base=seed)
+
+
+# ---- attention products ([Review] §5.6, Fig. 6) --------------------------------------
+
+def attention_qkv(heads: int, seq: int, head_dim: int, seed: int, n_outliers: int = 2):
+    """Q, K, V of one attention layer as bf16 bit patterns [heads, seq, head_dim]:
+    N(0, 1) entries, with n_outliers fixed channels of Q and K scaled by
+    U(5, 15) (query/key outliers persist per channel); seeds seed, seed+1, seed+2."""
+    out = []
+    for j, name in enumerate(("q", "k", "v")):
+        g = _rng(seed + j)
+        t = g.standard_normal((heads, seq, head_dim)).astype(np.float32)
+        if name != "v" and n_outliers:
+            ch = g.choice(head_dim, size=n_outliers, replace=False)
+            t[:, :, ch] *= g.uniform(5.0, 15.0, size=n_outliers).astype(np.float32)
+        out.append(f32_to_bf16_bits(t))
+    return tuple(out)
+
+
+def attention_probs(heads: int, seq_q: int, seq_k: int, seed: int) -> np.ndarray:
+    """Softmax-shaped attention probabilities [heads, seq_q, seq_k] fp32: each row
+    is softmax of N(0, 2^2) logits, computed in fp32 per head (seed + head)."""
+    p = np.empty((heads, seq_q, seq_k), np.float32)
+    for h in range(heads):
+        z = _rng(seed + h).standard_normal((seq_q, seq_k)).astype(np.float32) * np.float32(2.0)
+        z -= z.max(axis=1, keepdims=True)
+        e = np.exp(z, dtype=np.float32)
+        p[h] = e / e.sum(axis=1, keepdims=True, dtype=np.float32)
+    return p

@@ -219,6 +219,33 @@ sq_status sq_gemm_w8a8_ex(const int8_t* xq, const float* x_scale, sq_act_mode x_
                           int64_t M, int64_t N, int64_t K, const sq_epilogue* epi,
                           void* y, sq_dtype y_dt, sq_stream_t stream);
 
+/*
+ * sq_bmm_w8a8 -- a strided batch of int8 GEMMs: the batched matrix products
+ * of attention.  [Review] §5.6 / Fig. 6 (the compute-heavy operations of the
+ * Transformer block run in INT8: the linear layers and the batched matrix
+ * multiplications of attention; softmax, LayerNorm and the activation stay in
+ * floating point).  Entry z, with the contract of sq_gemm_w8a8:
+ *     y[z] = dequant( xq[z] [M, K] . wq[z]^T, x_scale[z], w_scale[z] )
+ *   scores  S = Q K^T: xq = codes of Q [S_q, d], wq = codes of K [S_k, d];
+ *           K's per-token steps play the per-output-channel role (w_mode
+ *           SQ_W_PER_CHANNEL) or one step per head (SQ_W_PER_TENSOR).
+ *   output  O = P V: xq = codes of P [S_q, S_k], wq = codes of V^T [d, S_k]
+ *           (one row per channel of V).
+ * Operand codes and steps come from sq_smooth_quantize_act with s = 1.
+ *   batch     number of entries (0 <= batch <= 65535)
+ *   *_stride  elements between consecutive entries; 0 repeats one tensor for
+ *             every entry.  xq_stride, wq_stride: multiples of 16 (always true
+ *             for contiguous operands, since K % 64 == 0).  y_stride and the
+ *             scale strides are free (an output entry that does not start on a
+ *             16-byte boundary is written element by element).
+ *   y_dt      SQ_F32, SQ_BF16 or SQ_I32.  Entries of y must not overlap.
+ */
+sq_status sq_bmm_w8a8(const int8_t* xq, int64_t xq_stride, const float* x_scale,
+                      int64_t xs_stride, sq_act_mode x_mode, const int8_t* wq,
+                      int64_t wq_stride, const float* w_scale, int64_t ws_stride,
+                      sq_weight_mode w_mode, int64_t batch, int64_t M, int64_t N, int64_t K,
+                      void* y, int64_t y_stride, sq_dtype y_dt, sq_stream_t stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* sq_status_string(sq_status status);
 

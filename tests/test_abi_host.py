@@ -199,3 +199,25 @@ def test_gemm_ex_validation():
     assert _gemm_ex((P, None, None, 1), ydt=0, M=0, xq=None, y=None) == 0
     # the plain entry point has no int8 output
     assert _gemm(ydt=2) == 3
+
+
+def _bmm(batch=2, M=4, N=4, K=64, xq=P, xqs=64 * 4, xs=P, xss=4, mode=0, wq=P, wqs=64 * 4,
+         ws=P, wss=4, wmode=0, y=P, ys=16, ydt=0):
+    return sq.lib().sq_bmm_w8a8(xq, xqs, xs, xss, mode, wq, wqs, ws, wss, wmode, batch, M, N, K,
+                                y, ys, ydt, None)
+
+
+def test_bmm_validation():
+    assert _bmm(batch=-1) == 2
+    assert _bmm(batch=65536) == 2
+    assert _bmm(K=96) == 2
+    assert _bmm(xqs=-16) == 2
+    assert _bmm(ydt=2) == 3               # no int8 output
+    assert _bmm(mode=4) == 7
+    assert _bmm(wmode=3) == 7
+    assert _bmm(xq=None) == 1
+    assert _bmm(ws=None) == 1
+    assert _bmm(xqs=8) == 5               # entry bases must stay 16-byte aligned
+    assert _bmm(wqs=24) == 5
+    assert _bmm(y=MIS) == 5
+    assert _bmm(batch=0, xq=None, wq=None, y=None) == 0

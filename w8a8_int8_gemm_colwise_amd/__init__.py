@@ -41,7 +41,7 @@ SETTINGS = {
     "O3": ("per_tensor", "static"),
 }
 EXPORTED = ("sq_calibrate", "sq_smooth_quantize_act", "sq_gemm_w8a8", "sq_gemm_w8a8_ex",
-            "sq_status_string", "sq_abi_version")
+            "sq_bmm_w8a8", "sq_status_string", "sq_abi_version")
 
 
 class SqEpilogue(ctypes.Structure):
@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
     L.sq_gemm_w8a8_ex.restype = ci
     L.sq_gemm_w8a8_ex.argtypes = [vp, vp, ci, vp, vp, ci, i64, i64, i64,
                                   ctypes.POINTER(SqEpilogue), vp, ci, vp]
+    L.sq_bmm_w8a8.restype = ci
+    L.sq_bmm_w8a8.argtypes = [vp, i64, vp, i64, ci, vp, i64, vp, i64, ci, i64, i64, i64, i64,
+                              vp, i64, ci, vp]
     L.sq_status_string.restype = ctypes.c_char_p
     L.sq_status_string.argtypes = [ci]
     L.sq_abi_version.restype = ci
@@ -234,4 +237,43 @@ def sq_gemm_w8a8_ex(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Te
     _check(lib().sq_gemm_w8a8_ex(_ptr(xq), _ptr(x_scale), _mode(mode), _ptr(wq), _ptr(w_scale),
                                  _wmode(w_mode), M, N, K, ctypes.byref(epi), _ptr(y), code,
                                  _stream(xq.device)))
+    return y
+
+
+def _stride(t: torch.Tensor | None, per_entry: int) -> int:
+    """Elements between batch entries of a contiguous [B, ...] tensor; 0 when a
+    single entry is shared by every batch entry."""
+    if t is None:
+        return 0
+    if t.dim() >= 1 and t.numel() == per_entry:
+        return 0
+    return per_entry
+
+
+def sq_bmm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor,
+                w_scale: torch.Tensor | None, mode="per_token", out_dtype: str = "bf16",
+                y: torch.Tensor | None = None, w_mode="per_channel") -> torch.Tensor:
+    """Batched int8 GEMM (the attention products): xq [B, M, K], wq [B, N, K]
+    (or [N, K] shared), x_scale [B, M] / [B, 1] / [1], w_scale [B, N] / [B, 1] /
+    [1]; returns y [B, M, N]."""
+    for t, n in ((xq, "xq"), (wq, "wq")):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() not in (2, 3):
+            raise ValueError(f"{n} must be a contiguous 2-D or 3-D GPU tensor")
+    B = xq.shape[0] if xq.dim() == 3 else wq.shape[0]
+    M, K = xq.shape[-2:]
+    N, K2 = wq.shape[-2:]
+    if K != K2:
+        raise ValueError("xq and wq disagree on K")
+    md, wm = _mode(mode), _wmode(w_mode)
+    code, tdt = _OUT[out_dtype]
+    if code == SQ_I8:
+        raise ValueError("the batched product has no int8 output")
+    if y is None:
+        y = torch.empty((B, M, N), dtype=tdt, device=xq.device)
+    xs_n = M if md == SQ_PER_TOKEN else 1
+    ws_n = N if wm == SQ_W_PER_CHANNEL else 1
+    _check(lib().sq_bmm_w8a8(
+        _ptr(xq), 0 if xq.dim() == 2 else M * K, _ptr(x_scale), _stride(x_scale, xs_n), md,
+        _ptr(wq), 0 if wq.dim() == 2 else N * K, _ptr(w_scale), _stride(w_scale, ws_n), wm,
+        B, M, N, K, _ptr(y), M * N, code, _stream(xq.device)))
     return y

@@ -114,7 +114,43 @@ sq_status sq_gemm_w8a8_ex(const int8_t* xq, const float* x_scale, sq_act_mode x_
         if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
     const int out = (y_dt == SQ_F32) ? 0 : (y_dt == SQ_BF16) ? 1 : (y_dt == SQ_I32) ? 2 : 3;
     return from_hip(sq::launch_gemm(xq, x_scale, x_mode == SQ_PER_TOKEN, wq, w_scale,
-                                    w_mode == SQ_W_PER_TENSOR, M, N, K, y, out, e,
+                                    w_mode == SQ_W_PER_TENSOR, M, N, K, y, out, e, sq::Batch{},
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+sq_status sq_bmm_w8a8(const int8_t* xq, int64_t xq_stride, const float* x_scale,
+                      int64_t xs_stride, sq_act_mode x_mode, const int8_t* wq,
+                      int64_t wq_stride, const float* w_scale, int64_t ws_stride,
+                      sq_weight_mode w_mode, int64_t batch, int64_t M, int64_t N, int64_t K,
+                      void* y, int64_t y_stride, sq_dtype y_dt, sq_stream_t stream) {
+    if (!valid_k(K) || !valid_rows(M) || !valid_rows(N)) return SQ_ERR_BAD_SHAPE;
+    if (batch < 0 || batch > 65535 || M * N > (int64_t(1) << 40)) return SQ_ERR_BAD_SHAPE;
+    if (xq_stride < 0 || xs_stride < 0 || wq_stride < 0 || ws_stride < 0 || y_stride < 0)
+        return SQ_ERR_BAD_SHAPE;
+    if (y_dt != SQ_F32 && y_dt != SQ_BF16 && y_dt != SQ_I32) return SQ_ERR_BAD_DTYPE;
+    if (x_mode != SQ_PER_TOKEN && x_mode != SQ_STATIC_PER_TENSOR &&
+        x_mode != SQ_DYNAMIC_PER_TENSOR)
+        return SQ_ERR_BAD_MODE;
+    if (w_mode != SQ_W_PER_CHANNEL && w_mode != SQ_W_PER_TENSOR) return SQ_ERR_BAD_MODE;
+    if (batch > 0 && M > 0 && N > 0) {
+        if (!xq || !wq || !y) return SQ_ERR_NULL_ARG;
+        if (y_dt != SQ_I32 && (!x_scale || !w_scale)) return SQ_ERR_NULL_ARG;
+    }
+    if (xq_stride % 16 != 0 || wq_stride % 16 != 0) return SQ_ERR_ALIGNMENT;
+    const void* ptrs[] = {xq, x_scale, wq, w_scale, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
+    if (batch == 0) return SQ_OK;
+    sq::Batch b;
+    b.count = batch;
+    b.a = xq_stride;
+    b.b = wq_stride;
+    b.sx = xs_stride;
+    b.sw = ws_stride;
+    b.y = y_stride;
+    const int out = (y_dt == SQ_F32) ? 0 : (y_dt == SQ_BF16) ? 1 : 2;
+    return from_hip(sq::launch_gemm(xq, x_scale, x_mode == SQ_PER_TOKEN, wq, w_scale,
+                                    w_mode == SQ_W_PER_TENSOR, M, N, K, y, out, sq::Epi{}, b,
                                     reinterpret_cast<hipStream_t>(stream)));
 }
 

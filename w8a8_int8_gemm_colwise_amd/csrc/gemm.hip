@@ -58,6 +58,23 @@ __device__ __forceinline__ int lds_off_k(int row, int chunk) {
 
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2, kOutI8 = 3 };
 
+template <int OUT>
+constexpr int out_bytes() { return OUT == kOutBF16 ? 2 : OUT == kOutI8 ? 1 : 4; }
+
+// Batch entry blockIdx.y of a strided batch (see Batch): offsets of the kernel's
+// operand, scale and output pointers, applied at kernel entry.
+#define SQ_APPLY_BATCH(OUT_)                                                        \
+    do {                                                                            \
+        const int64_t bz_ = blockIdx.y;                                             \
+        if (bz_ > 0) {                                                              \
+            A += bz_ * bat.a;                                                       \
+            B += bz_ * bat.b;                                                       \
+            if (sx) sx += bz_ * bat.sx;                                             \
+            if (sw) sw += bz_ * bat.sw;                                             \
+            Y = static_cast<int8_t*>(Y) + bz_ * bat.y * out_bytes<OUT_>();          \
+        }                                                                           \
+    } while (0)
+
 // Fused epilogue on a dequantized value y (see Epi): bias, then ReLU to +0.
 __device__ __forceinline__ float bias_relu(float y, bool has_bias, float b, int relu) {
     if (has_bias) y = y + b;
@@ -171,7 +188,8 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
-    int M, int N, int K, Epi epi) {
+    int M, int N, int K, Epi epi, Batch bat) {
+    SQ_APPLY_BATCH(OUT);
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     static_assert(T::LA * T::kThreads == BM * kChunksPerRow, "A tile divides over threads");
     static_assert(T::LB * T::kThreads == BN * kChunksPerRow, "B tile divides over threads");
@@ -277,28 +295,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
                const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, const Epi& epi,
-                    hipStream_t stream) {
+                    const Batch& bat, hipStream_t stream) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const dim3 grid(tiles), block(T::kThreads);
+    const dim3 grid(tiles, static_cast<unsigned>(bat.count)), block(T::kThreads);
     const int pt = per_token ? 1 : 0;
     const int wpt = w_per_tensor ? 1 : 0;
     switch (out) {
         case kOutF32:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutF32><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
         case kOutBF16:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutBF16><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
         case kOutI8:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutI8><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
         default:
             gemm_kernel<BM, BN, WAVES_M, WAVES_N, kOutI32><<<grid, block, 0, stream>>>(
-                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+                xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
     }
     return hipGetLastError();
@@ -318,9 +336,6 @@ hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* 
 // The dequantization is the library's fixed order: f = s_x * s_w, then
 // y = float(acc) * f, then bias and ReLU, then the output type (bf16 rounding,
 // or the next linear's int8 code).
-template <int OUT>
-constexpr int out_bytes() { return OUT == kOutBF16 ? 2 : OUT == kOutI8 ? 1 : 4; }
-
 template <int OUT, int TN>
 constexpr int epi_pitch() { return TN * 32 * out_bytes<OUT>() + (out_bytes<OUT>() == 4 ? 16 : 8); }
 
@@ -339,7 +354,9 @@ __device__ __forceinline__ void store_tile_t(const v16i (&acc)[TM][TN], int row0
     static_assert((32 * CPR) % 64 == 0, "whole chunks per lane");
     const int fr = lane & 31;
     const int h = lane >> 5;
-    const bool vec_ok = ((static_cast<int64_t>(N) * ES) % 16) == 0;
+    // 16-byte stores need 16-byte rows and base (a batch entry may start anywhere)
+    const bool vec_ok = ((static_cast<int64_t>(N) * ES) % 16) == 0 &&
+                        (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const float dx = (OUT == kOutI32) ? 0.0f : sxs[i * 32 + fr];
@@ -477,7 +494,8 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OUT>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
-    int M, int N, int K, Epi epi) {
+    int M, int N, int K, Epi epi, Batch bat) {
+    SQ_APPLY_BATCH(OUT);
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     static_assert(WAVES_M * WAVES_N == 8, "two groups of four waves");
     constexpr int kRows = BM + BN;
@@ -623,27 +641,27 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
 hipError_t run_pp(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
                   const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, const Epi& epi,
-                    hipStream_t stream) {
+                    const Batch& bat, hipStream_t stream) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const dim3 grid(tiles), block(512);
+    const dim3 grid(tiles, static_cast<unsigned>(bat.count)), block(512);
     const int pt = per_token ? 1 : 0;
     const int wpt = w_per_tensor ? 1 : 0;
     switch (out) {
         case kOutF32:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutF32>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
         case kOutBF16:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutBF16>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
         case kOutI8:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutI8>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
         default:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutI32>
-                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+                <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
     }
     return hipGetLastError();
@@ -688,7 +706,8 @@ template <int MT, int WPB, int ST, int OUT>
 __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
-    int M, int N, int K, Epi epi) {
+    int M, int N, int K, Epi epi, Batch bat) {
+    SQ_APPLY_BATCH(OUT);
     using S = Skinny<MT, WPB, ST>;
     static_assert(ST >= 2 && ST <= 3, "2 or 3 stages");
     __shared__ __attribute__((aligned(1024))) int8_t ring[S::kRing];
@@ -776,22 +795,22 @@ __global__ __launch_bounds__(64 * WPB) void gemm_skinny_kernel(
 template <int MT, int WPB, int ST>
 hipError_t run_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
                       const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, const Epi& epi,
-                    hipStream_t stream) {
-    const dim3 grid((N + 31) / 32), block(64 * WPB);
+                    const Batch& bat, hipStream_t stream) {
+    const dim3 grid((N + 31) / 32, static_cast<unsigned>(bat.count)), block(64 * WPB);
     const int pt = per_token ? 1 : 0;
     const int wpt = w_per_tensor ? 1 : 0;
     switch (out) {
         case kOutF32:
-            gemm_skinny_kernel<MT, WPB, ST, kOutF32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+            gemm_skinny_kernel<MT, WPB, ST, kOutF32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
         case kOutBF16:
-            gemm_skinny_kernel<MT, WPB, ST, kOutBF16><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+            gemm_skinny_kernel<MT, WPB, ST, kOutBF16><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
         case kOutI8:
-            gemm_skinny_kernel<MT, WPB, ST, kOutI8><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+            gemm_skinny_kernel<MT, WPB, ST, kOutI8><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
         default:
-            gemm_skinny_kernel<MT, WPB, ST, kOutI32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi);
+            gemm_skinny_kernel<MT, WPB, ST, kOutI32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
             break;
     }
     return hipGetLastError();
@@ -802,13 +821,13 @@ hipError_t run_skinny(const int8_t* xq, const float* sx, bool per_token, const i
 // eight when there are few; two 32-row X tiles take three stages.
 hipError_t launch_skinny(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
                          const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, const Epi& epi,
-                    hipStream_t stream) {
+                    const Batch& bat, hipStream_t stream) {
     const int blocks = (N + 31) / 32;
     if (M <= 32) {
-        if (blocks >= 512) return run_skinny<1, 4, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, epi, stream);
-        return run_skinny<1, 8, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, epi, stream);
+        if (blocks >= 512) return run_skinny<1, 4, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, epi, bat, stream);
+        return run_skinny<1, 8, 2>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, epi, bat, stream);
     }
-    return run_skinny<2, 4, 3>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, epi, stream);
+    return run_skinny<2, 4, 3>(xq, sx, per_token, wq, sw, w_per_tensor, M, N, K, y, out, epi, bat, stream);
 }
 
 }  // namespace
@@ -816,15 +835,15 @@ hipError_t launch_skinny(const int8_t* xq, const float* sx, bool per_token, cons
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
                        const int8_t* wq, const float* w_scale, bool w_per_tensor, int64_t M,
                        int64_t N, int64_t K, void* y, int out_kind, const Epi& epi,
-                       hipStream_t stream) {
+                       const Batch& bat, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     if (M <= 64) {
         // decode shapes: stream W once, K split over the waves of a block
         if (K % 128 == 0 && N * K < (int64_t(1) << 31)) {
-            return launch_skinny(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, stream);
+            return launch_skinny(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, bat, stream);
         }
-        return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, stream);
+        return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, bat, stream);
     }
     // ping-pong kernels: K a multiple of the 128-byte stage of the 256x128
     // tile, operand offsets in int32
@@ -838,14 +857,14 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
         const int64_t cost_mid = ((t_mid + 255) / 256) * 105;
         if (cost_big <= cost_mid)
             return run_pp<256, 256, 2, 4, 64, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
-                                                 out_kind, epi, stream);
+                                                 out_kind, epi, bat, stream);
         return run_pp<256, 128, 4, 2, 128, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
-                                              out_kind, epi, stream);
+                                              out_kind, epi, bat, stream);
     }
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 127) / 128);
     if (big_tiles >= 256)
-        return run<256, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, stream);
-    return run<128, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, stream);
+        return run<256, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, bat, stream);
+    return run<128, 128, 2, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, bat, stream);
 }
 
 }  // namespace sq

@@ -42,12 +42,20 @@ struct Epi {
     int relu = 0;
 };
 
+// Strided batch of independent GEMMs (the attention products): entry z uses
+// A + z*a, B + z*b, x_scale + z*sx, w_scale + z*sw and writes Y + z*y (all in
+// elements).  count = 1 is the plain GEMM.
+struct Batch {
+    int64_t count = 1;
+    int64_t a = 0, b = 0, sx = 0, sw = 0, y = 0;
+};
+
 // Int8 GEMM with dequantizing epilogue.  out_kind: 0 = f32, 1 = bf16, 2 = i32
 // (raw accumulators, epilogue unused), 3 = i8 (requantized for the next linear).
 // w_per_tensor: w_scale[0] is the step of every output channel.
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
                        const int8_t* wq, const float* w_scale, bool w_per_tensor, int64_t M,
                        int64_t N, int64_t K, void* y, int out_kind, const Epi& epi,
-                       hipStream_t stream);
+                       const Batch& bat, hipStream_t stream);
 
 }  // namespace sq
