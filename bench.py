@@ -35,7 +35,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SRC = os.path.join(ROOT, "w8a8_int8_gemm_colwise_amd", "csrc", "gemm.hip")
 
-WORKLOADS = {"opt6.7b": 2, "decode70b": 3, "opt175b": 4, "ln8192": 5, "single512": 1}
+WORKLOADS = {"opt6.7b": 2, "decode70b": 3, "opt175b": 4, "ln8192": 5, "single512": 1,
+             "attn6.7b": None}
+# OPT-6.7B self-attention at 2048 tokens: 32 heads of dimension 128
+ATTN_HEADS, ATTN_SEQ, ATTN_HD = 32, 2048, 128
 
 
 def _bytes_of(dt: str) -> int:
@@ -103,6 +106,177 @@ def cpu_baseline(workload, max_tokens: int = 256, w_mode: str = "per_channel",
                        f"oracle wall time ({t_total:.1f} s)")}
 
 
+def _attn_inputs(H, S, D):
+    """Q, K, V^T (bf16 [H,S,D], [H,S,D], [H,D,S]) and the softmax output P
+    (bf16 [H,S,S]; the precision map keeps softmax in 16-bit float)."""
+    import datagen
+    q, k, v = datagen.attention_qkv(H, S, D, seed=6700)
+    vt = np.ascontiguousarray(np.swapaxes(v, 1, 2))
+    p = datagen.f32_to_bf16_bits(datagen.attention_probs(H, S, S, seed=6800))
+    return q, k, vt, p
+
+
+def cpu_baseline_attention(heads: int):
+    """Time the CPU oracle on the attention step for the first ``heads`` heads
+    (per-token quantization of Q, K, P and V^T rows, S = Q K^T and O = P V with
+    bf16 outputs)."""
+    import oracle
+
+    H, S, D = ATTN_HEADS, ATTN_SEQ, ATTN_HD
+    q, k, vt, p = _attn_inputs(H, S, D)
+    f = oracle.bf16_to_f32
+
+    def rows(t):
+        ones = np.ones(t.shape[1], np.float32)
+        c, st, _ = oracle.smooth_quantize_act(t, s=ones)
+        return c, st
+
+    t0 = time.perf_counter()
+    for h in range(heads):
+        qq, qs = rows(f(q[h]))
+        kq, ks = rows(f(k[h]))
+        oracle.gemm_w8a8(qq, qs, kq, ks, out="bf16")
+        pq, ps = rows(f(p[h]))
+        vq, vs = rows(f(vt[h]))
+        oracle.gemm_w8a8(pq, ps, vq, vs, out="bf16")
+    t = time.perf_counter() - t0
+    ops = heads * 2 * (2.0 * S * S * D)
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"{heads} of {H} heads: per-token quantization of Q, K, P, V^T rows, "
+                       f"S = Q K^T and O = P V with bf16 outputs; value = BMM ops of the sample "
+                       f"/ oracle wall time ({t:.1f} s)")}
+
+
+def bench_attention(args, attain_fn):
+    """The attention products of one OPT-6.7B layer at 2048 tokens: per-token
+    int8 codes of Q, K (rows of [H*S, D]), S = Q K^T (bf16); per-token codes
+    of P (rows of [H*S, S]) and per-channel codes of V (rows of V^T, [H*D, S]),
+    O = P V (bf16).  Softmax itself is not on the int8 path (P is an input)."""
+    import torch
+
+    import w8a8_int8_gemm_colwise_amd as sq
+
+    H, S, D = ATTN_HEADS, ATTN_SEQ, ATTN_HD
+    dev = torch.device("cuda:0")
+    q, k, vt, p = _attn_inputs(H, S, D)
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    tq, tk, tvt, tp = bf(q).view(H * S, D), bf(k).view(H * S, D), bf(vt).view(H * D, S), \
+        bf(p).view(H * S, S)
+    del q, k, vt, p
+    f32 = dict(dtype=torch.float32, device=dev)
+    i8 = dict(dtype=torch.int8, device=dev)
+    ones_d, ones_s = torch.ones(D, **f32), torch.ones(S, **f32)
+    qq, kq = torch.empty((H * S, D), **i8), torch.empty((H * S, D), **i8)
+    pq, vq = torch.empty((H * S, S), **i8), torch.empty((H * D, S), **i8)
+    qs, ks, ps, vs = (torch.empty(H * S, **f32), torch.empty(H * S, **f32),
+                      torch.empty(H * S, **f32), torch.empty(H * D, **f32))
+    s_out = torch.empty((H, S, S), dtype=torch.bfloat16, device=dev)
+    o_out = torch.empty((H, S, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    calls = ["quant_qk", "bmm_qk", "quant_pv", "bmm_pv"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        sq.sq_smooth_quantize_act(tq, ones_d, xq=qq, x_scale=qs)
+        sq.sq_smooth_quantize_act(tk, ones_d, xq=kq, x_scale=ks)
+        mark(1)
+        sq.sq_bmm_w8a8(qq.view(H, S, D), qs.view(H, S), kq.view(H, S, D), ks.view(H, S),
+                       out_dtype="bf16", y=s_out)
+        mark(2)
+        sq.sq_smooth_quantize_act(tp, ones_s, xq=pq, x_scale=ps)
+        sq.sq_smooth_quantize_act(tvt, ones_s, xq=vq, x_scale=vs)
+        mark(3)
+        sq.sq_bmm_w8a8(pq.view(H, S, S), ps.view(H, S), vq.view(H, D, S), vs.view(H, D),
+                       out_dtype="bf16", y=o_out)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for kk in range(args.steps):
+        step(evs[kk])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t = np.zeros(4)
+    for e in evs:
+        for i in range(4):
+            t[i] += e[i].elapsed_time(e[i + 1]) * 1e-3
+    t /= args.steps
+    ms = elapsed / args.steps * 1e3
+    bmm_ops = 2.0 * S * S * D * H            # each product
+    # algorithmic bytes: read the bf16 input + write codes + per-row step
+    b_qk = 2 * (H * S * D * 3 + 4 * H * S + 4 * D)
+    b_pv = (H * S * S * 3 + 4 * H * S + 4 * S) + (H * D * S * 3 + 4 * H * D + 4 * S)
+    b_bmm1 = 2 * H * S * D + 8 * H * S + 2 * H * S * S
+    b_bmm2 = H * S * S + H * D * S + 4 * H * S + 4 * H * D + 2 * H * S * D
+    alg = [b_qk, b_bmm1, b_pv, b_bmm2]
+    per = {c: {"us": round(t[i] * 1e6, 2), "GBs_alg": round(alg[i] / t[i] / 1e9, 1)}
+           for i, c in enumerate(calls)}
+    per["bmm_qk"]["TOPS"] = round(bmm_ops / t[1] / 1e12, 1)
+    per["bmm_pv"]["TOPS"] = round(bmm_ops / t[3] / 1e12, 1)
+    # every call here moves far more bytes than the int8 MFMA needs time for
+    # (ridge 5.0e15 / 8e12 = 625 ops per byte; S = Q K^T has 2*D*S*S / 2*S*S = 128)
+    i_dom = int(np.argmax(t))
+    names = {"quant_qk": "sq_smooth_quantize_act (Q, K)", "bmm_qk": "sq_bmm_w8a8 (S = Q K^T)",
+             "quant_pv": "sq_smooth_quantize_act (P, V^T)", "bmm_pv": "sq_bmm_w8a8 (O = P V)"}
+    ach = alg[i_dom] / t[i_dom] / 1e9
+    launches = 1 if calls[i_dom].startswith("bmm") else 2
+    roof = {"kernel": names[calls[i_dom]], "bound": "hbm", "achieved": round(ach, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+            "traffic": None, "launches_per_step": launches,
+            "avg_launch_us": round(t[i_dom] / launches * 1e6, 2),
+            "alg_bytes_per_launch": alg[i_dom] / launches}
+    attain = attain_fn(dev)
+    if attain:
+        roof["attainable"] = attain["hbm_copy_GBs"]
+        roof["frac_attainable"] = round(ach / attain["hbm_copy_GBs"], 4)
+    out = {
+        "metric": "W8A8 GEMM INT8 TOPS (% MFMA peak) + fused quantize GB/s (% HBM peak)",
+        "value": round(2 * bmm_ops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic (seeded; Q, K with 2 outlier channels x U(5,15); P = softmax of "
+                "N(0, 2^2) logits; bf16 inputs)",
+        "config": {"workload": f"attention of OPT-6.7B: {H} heads x {S} tokens, head dim {D}",
+                   "act_scale": "per_token (Q, K, P rows); per_channel (V, rows of V^T)",
+                   "y_dtype": "bf16",
+                   "step": "quantize Q, K; S = Q K^T; quantize P, V^T; O = P V"},
+        "roofline": roof,
+        "per_call": per,
+    }
+    if attain:
+        out["attainable"] = attain
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_attention(args.cpu_heads)
+    return out
+
+
+def _attainable(args):
+    def fn(dev):
+        if args.no_probes:
+            return None
+        from w8a8_int8_gemm_colwise_amd import probes
+        return {"mfma_i8_TOPS": round(probes.mfma_i8_tops(dev), 1),
+                "hbm_read_GBs": round(probes.hbm_read_gbs(dev), 1),
+                "hbm_copy_GBs": round(probes.hbm_copy_gbs(dev), 1),
+                "how": "libsqprobe: int8 MFMA loop on operands rne(N(0,40^2)) clipped to "
+                       "+-127; streaming read of 1 GiB; copy of 512 MiB (read + written bytes)"}
+    return fn
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +289,8 @@ def main():
                          "per token (default); O1-O3 = the per-tensor weight settings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-heads", type=int, default=32,
+                    help="attn6.7b: heads of the CPU oracle's sample")
     ap.add_argument("--fuse-ffn", action="store_true",
                     help="opt6.7b: fc1's GEMM epilogue applies ReLU and writes fc2's int8 input "
                          "codes (fc2's smoothing factor and static step), so fc2 has no "
@@ -129,6 +305,9 @@ def main():
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU sharding).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "attn6.7b":
+        print(json.dumps(bench_attention(args, _attainable(args))), flush=True)
+        return
 
     import torch
 
@@ -284,14 +463,7 @@ def main():
     value = tot_ops / (ms_per_step * 1e-3) / 1e12
 
     # attainable ceilings on this machine (after the timed region)
-    attain = None
-    if not args.no_probes:
-        from w8a8_int8_gemm_colwise_amd import probes
-        attain = {"mfma_i8_TOPS": round(probes.mfma_i8_tops(dev), 1),
-                  "hbm_read_GBs": round(probes.hbm_read_gbs(dev), 1),
-                  "hbm_copy_GBs": round(probes.hbm_copy_gbs(dev), 1),
-                  "how": "libsqprobe: int8 MFMA loop on operands rne(N(0,40^2)) clipped to "
-                         "+-127; streaming read of 1 GiB; copy of 512 MiB (read + written bytes)"}
+    attain = _attainable(args)(dev)
 
     # dominant kernel by time: the GEMM unless the HBM-bound calls take longer
     tg, tc, ta = t_gemm.sum(), t_cal.sum(), t_act.sum()

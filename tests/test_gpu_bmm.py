@@ -1,8 +1,8 @@
 """GPU parity of the batched int8 products of attention (sq_bmm_w8a8;
 [Review] §5.6, Fig. 6: the batched matrix multiplications of attention run in
 INT8 like the linear layers) against the oracle, bit for bit: small batches
-reaching every GEMM kernel (ping-pong, skinny, register-staged for head
-dimension 64), every step granularity and shared (stride 0) operands; and the
+reaching every GEMM kernel (short K for head dimensions 64, 128 and 256,
+ping-pong, skinny, register-staged), every step granularity and shared (stride 0) operands; and the
 OPT-6.7B-shaped attention (32 heads, 2048 tokens, head dimension 128): scores
 S = Q K^T and output O = P V with operands quantized per token by
 sq_smooth_quantize_act (s = 1), checked on sampled heads.
@@ -37,10 +37,12 @@ def _oracle_rows(t3):
 
 CASES = [
     # B, M, N, K, x mode, w mode, shared w
-    (3, 257, 300, 128, "per_token", "per_channel", False),   # ping-pong
-    (2, 300, 96, 256, "per_token", "per_channel", True),     # shared second operand
+    (3, 257, 300, 128, "per_token", "per_channel", False),   # short K (head dim 128)
+    (2, 300, 96, 256, "per_token", "per_channel", True),     # short K 256, shared operand
+    (2, 200, 300, 384, "per_token", "per_channel", False),   # ping-pong
     (4, 40, 513, 128, "per_token", "per_tensor", False),     # skinny
-    (3, 130, 70, 64, "per_token", "per_channel", False),     # head dim 64: register-staged
+    (3, 130, 70, 64, "per_token", "per_channel", False),     # short K (head dim 64)
+    (2, 150, 90, 192, "per_token", "per_channel", False),    # register-staged (K % 128 != 0)
     (2, 1, 2048, 128, "per_token", "per_channel", False),    # one query token (decode)
     (2, 96, 128, 512, "dynamic_per_tensor", "per_tensor", False),
 ]

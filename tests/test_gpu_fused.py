@@ -17,10 +17,12 @@ from sqcase import assert_same, dev, sample_idx, say, to_dev, to_np
 pytestmark = pytest.mark.gpu
 
 SHAPES = [
-    # M, N, K: ping-pong 256x128 and 256x256 tiles, skinny (M <= 64), fallback (K % 128 != 0);
+    # M, N, K: ping-pong 256x128 and 256x256 tiles, short K (K = 128, 256), skinny (M <= 64),
+    # fallback (K % 128 != 0);
     # N a multiple of 64 where the unfused graph is compared too
     (257, 513, 1024),
     (300, 1100, 256),
+    (200, 320, 128),
     (290, 2048, 512),
     (64, 200, 512),
     (1, 96, 2048),

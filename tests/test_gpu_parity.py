@@ -57,6 +57,11 @@ RAGGED = [
     (6, 64, 49152, "bf16", "bf16", "per_token", False, 0.5),
     (3, 64, 16384 + 64, "bf16", "bf16", "per_token", True, 0.5),
     (4, 40, 133120, "bf16", "bf16", "per_token", False, 0.5),
+    # short-K kernel (whole K in LDS): K = 64, 128, 256 with ragged M and N
+    (200, 300, 64, "bf16", "bf16", "per_token", False, 0.5),
+    (129, 257, 128, "f32", "bf16", "static", True, 0.5),
+    (300, 130, 256, "bf16", "bf16", "per_token", False, 0.5),
+    (150, 70, 128, "bf16", "f32", "static", False, 0.5),
     # skinny-M (decode) kernel: one and two 32-row tiles, static scale, ragged N
     (64, 72, 1152, "bf16", "bf16", "static", False, 0.5),
     (1, 33, 256, "f32", "f32", "static", True, 0.5),

@@ -270,6 +270,8 @@ def sq_bmm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor
         raise ValueError("the batched product has no int8 output")
     if y is None:
         y = torch.empty((B, M, N), dtype=tdt, device=xq.device)
+    elif y.dtype != tdt or not y.is_cuda or not y.is_contiguous() or y.numel() != B * M * N:
+        raise ValueError(f"y must be a contiguous GPU tensor of {B}x{M}x{N} {tdt}")
     xs_n = M if md == SQ_PER_TOKEN else 1
     ws_n = N if wm == SQ_W_PER_CHANNEL else 1
     _check(lib().sq_bmm_w8a8(

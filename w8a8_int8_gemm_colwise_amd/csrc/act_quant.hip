@@ -254,6 +254,83 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
     }
 }
 
+// Short rows (plain mode, K <= 256: at most 32 chunks).  A wave quantizes
+// 64 / SG rows at once, SG lanes per row (SG = the chunk count rounded up to a
+// power of two): lane l owns chunk l % SG of row l / SG, so its s_k and
+// RN(1/s_k) stay in registers, and the row maximum is reduced within the
+// lane's SG-lane group.  The next group of rows is in flight while the current
+// one is quantized.  Per element the arithmetic is that of act_quant_kernel.
+template <typename T, bool STATIC, int SG>
+__global__ __launch_bounds__(256) void act_quant_rows_kernel(
+    const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
+    const float* __restrict__ static_scale, int8_t* __restrict__ xq,
+    float* __restrict__ x_scale, float* __restrict__ rowmax) {
+    constexpr int R = 64 / SG;
+    const int lane = threadIdx.x & 63;
+    const int r = lane / SG, c = lane % SG;
+    const int64_t chunks = K / kChunk;
+    const bool act = c < chunks;
+    const int64_t W = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
+    const int64_t groups = (M + R - 1) / R;
+    int64_t g = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+
+    RawChunk<T> cur{}, nxt{};
+    auto fetch = [&](int64_t gg, RawChunk<T>& rc) {
+        const int64_t m = gg * R + r;
+        if (act && m < M) rc = load_raw(x + m * K, c);
+    };
+    if (g < groups) fetch(g, cur);
+    float c0[kChunk], c1[kChunk];
+    if (act) {
+        load_chunk(s, c, c0);
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) c1[e] = 1.0f / c0[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) c0[e] = c1[e] = 1.0f;
+    }
+    float d_static = 0.0f, rd_static = 0.0f;
+    if (STATIC) {
+        d_static = *static_scale;
+        rd_static = 1.0f / d_static;
+    }
+    for (; g < groups; g += W) {
+        if (g + W < groups) fetch(g + W, nxt);
+        const int64_t m = g * R + r;
+        const bool live = act && m < M;
+        float v[kChunk];
+        unpack(cur, v);
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) v[e] = div_rn(v[e], c0[e], c1[e]);
+        float d, rd;
+        if (STATIC) {
+            d = d_static;
+            rd = rd_static;
+        } else {
+            float mx = 0.0f;
+            if (live) {
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) mx = fmaxf(mx, fabsf(v[e]));
+            }
+#pragma unroll
+            for (int o = SG / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            d = step_from_absmax(mx);
+            rd = 1.0f / d;
+            if (c == 0 && m < M) {
+                if (rowmax) rowmax[m] = mx;
+                else x_scale[m] = d;
+            }
+        }
+        if ((STATIC || rowmax == nullptr) && live) {
+            int q[kChunk];
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[e], d, rd);
+            *reinterpret_cast<uint2*>(xq + m * K + c * kChunk) = pack8(q);
+        }
+        cur = nxt;
+    }
+}
+
 // Any K: the row is re-read from memory for each sweep (mostly L2 hits).
 // 256 lanes, so LayerNorm partials are canonical here too.
 template <typename T, bool LN>
@@ -379,9 +456,24 @@ hipError_t run_stream(const ActArgs& a, hipStream_t stream) {
 }
 
 
+template <typename T, bool STATIC, int SG>
+hipError_t run_rows(const ActArgs& a, hipStream_t stream) {
+    // four waves per block, at most eight blocks per CU; each wave walks
+    // groups of 64 / SG rows
+    const int64_t groups = (a.M + 64 / SG - 1) / (64 / SG);
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>((groups + 3) / 4, 256 * 8));
+    act_quant_rows_kernel<T, STATIC, SG><<<grid, 256, 0, stream>>>(
+        static_cast<const T*>(a.x), a.M, a.K, a.s, a.static_scale, a.xq, a.x_scale, a.rowmax);
+    return hipGetLastError();
+}
+
 template <typename T, bool STATIC>
 hipError_t dispatch_plain(const ActArgs& a, hipStream_t stream) {
     const int64_t chunks = a.K / kChunk;
+    // short rows: several rows per wave
+    if (chunks <= 8) return run_rows<T, STATIC, 8>(a, stream);
+    if (chunks <= 16) return run_rows<T, STATIC, 16>(a, stream);
+    if (chunks <= 32) return run_rows<T, STATIC, 32>(a, stream);
     // rows up to 2048 chunks: one or two 16-byte loads per lane and row with the
     // per-column constants cached and the next row prefetched (measured: one
     // prefetched row beats deeper rings on the MI355X); longer rows:

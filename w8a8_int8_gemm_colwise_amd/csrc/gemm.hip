@@ -339,7 +339,7 @@ hipError_t run(const int8_t* xq, const float* sx, bool per_token, const int8_t* 
 template <int OUT, int TN>
 constexpr int epi_pitch() { return TN * 32 * out_bytes<OUT>() + (out_bytes<OUT>() == 4 ? 16 : 8); }
 
-template <int OUT, int TM, int TN>
+template <int OUT, int TM, int TN, bool FUSED>
 __device__ __forceinline__ void store_tile_t(const v16i (&acc)[TM][TN], int row0, int col0,
                                              int lane, const float* sxs, const float* sws,
                                              const float* bcs, const float* scs,
@@ -351,80 +351,120 @@ __device__ __forceinline__ void store_tile_t(const v16i (&acc)[TM][TN], int row0
     constexpr int PITCH = epi_pitch<OUT, TN>();
     constexpr int CPR = SEG / 16;                  // 16-byte chunks per row
     constexpr int EPC = 16 / ES;                   // elements per chunk
-    static_assert((32 * CPR) % 64 == 0, "whole chunks per lane");
+    constexpr int NQ = 32 * CPR / 64;              // chunks per lane per 32-row slice
+    static_assert(NQ * 64 == 32 * CPR, "whole chunks per lane");
     const int fr = lane & 31;
     const int h = lane >> 5;
-    // 16-byte stores need 16-byte rows and base (a batch entry may start anywhere)
-    const bool vec_ok = ((static_cast<int64_t>(N) * ES) % 16) == 0 &&
-                        (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+    const bool hb = FUSED && e.bias != nullptr;
+    const int relu = FUSED ? e.relu : 0;
+    // whole slices go out as 16-byte stores when rows and base are 16-byte
+    // aligned (a batch entry may start anywhere) and the slice is in range
+    const bool cols_in = ((static_cast<int64_t>(N) * ES) % 16) == 0 &&
+                         (reinterpret_cast<uintptr_t>(Y) & 15) == 0 && col0 + TN * 32 <= N;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const float dx = (OUT == kOutI32) ? 0.0f : sxs[i * 32 + fr];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
+            // the lane's 16 columns of this 32-column block: c = j*32 + 8g + 4h + t,
+            // taken GB groups g at a time; every LDS read of a batch is issued
+            // before any of its values is used
+            constexpr int GB = 2;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g0 = 0; g0 < 4; g0 += GB) {
+            float4 w4[GB], b4[GB], s4[GB], r4[GB];
+#pragma unroll
+            for (int gg = 0; gg < GB; ++gg) {
+                const int g = g0 + gg;
+                const int c = j * 32 + 8 * g + 4 * h;
+                if (OUT != kOutI32) w4[gg] = *reinterpret_cast<const float4*>(sws + c);
+                if (OUT != kOutI32 && FUSED) b4[gg] = *reinterpret_cast<const float4*>(bcs + c);
+                if (OUT == kOutI8) {
+                    s4[gg] = *reinterpret_cast<const float4*>(scs + c);
+                    r4[gg] = *reinterpret_cast<const float4*>(rcs + c);
+                }
+            }
+#pragma unroll
+            for (int gg = 0; gg < GB; ++gg) {
+                const int g = g0 + gg;
                 const int c = j * 32 + 8 * g + 4 * h;  // first of the lane's 4 columns
                 int8_t* dst = scratch + fr * PITCH + c * ES;
                 if (OUT == kOutI32) {
                     v4i v;
-                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+                    for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * g + t];
                     *reinterpret_cast<v4i*>(dst) = v;
+                    continue;
+                }
+                const float dw[4] = {w4[gg].x, w4[gg].y, w4[gg].z, w4[gg].w};
+                float y[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float f = dx * dw[t];
+                    y[t] = static_cast<float>(acc[i][j][4 * g + t]) * f;
+                }
+                if constexpr (FUSED) {
+                    const float bb[4] = {b4[gg].x, b4[gg].y, b4[gg].z, b4[gg].w};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) y[t] = bias_relu(y[t], hb, bb[t], relu);
+                }
+                if (OUT == kOutF32) {
+                    *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+                } else if (OUT == kOutBF16) {
+                    typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+                    bf4 bv;
+                    for (int t = 0; t < 4; ++t) bv[t] = static_cast<__bf16>(y[t]);
+                    *reinterpret_cast<bf4*>(dst) = bv;
                 } else {
-                    const float4 w = *reinterpret_cast<const float4*>(sws + c);
-                    const float dw[4] = {w.x, w.y, w.z, w.w};
-                    const bool hb = e.bias != nullptr;
-                    float4 bv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    if (hb) bv = *reinterpret_cast<const float4*>(bcs + c);
-                    const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
-                    float y[4];
+                    const bool hs = e.next_s != nullptr;
+                    const float ss[4] = {s4[gg].x, s4[gg].y, s4[gg].z, s4[gg].w};
+                    const float rr[4] = {r4[gg].x, r4[gg].y, r4[gg].z, r4[gg].w};
+                    uint32_t packed = 0;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const float f = dx * dw[t];
-                        y[t] = bias_relu(static_cast<float>(acc[i][j][4 * g + t]) * f, hb, bb[t],
-                                         e.relu);
+                        const int q = requant_code(y[t], hs, ss[t], rr[t], D, rD);
+                        packed |= (static_cast<uint32_t>(q) & 0xffu) << (8 * t);
                     }
-                    if (OUT == kOutF32) {
-                        *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
-                    } else if (OUT == kOutBF16) {
-                        typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
-                        bf4 b;
-                        for (int t = 0; t < 4; ++t) b[t] = static_cast<__bf16>(y[t]);
-                        *reinterpret_cast<bf4*>(dst) = b;
-                    } else {
-                        const bool hs = e.next_s != nullptr;
-                        const float4 sv = *reinterpret_cast<const float4*>(scs + c);
-                        const float4 rv = *reinterpret_cast<const float4*>(rcs + c);
-                        const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
-                        const float rr[4] = {rv.x, rv.y, rv.z, rv.w};
-                        uint32_t packed = 0;
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            const int q = requant_code(y[t], hs, ss[t], rr[t], D, rD);
-                            packed |= (static_cast<uint32_t>(q) & 0xffu) << (8 * t);
-                        }
-                        *reinterpret_cast<uint32_t*>(dst) = packed;
-                    }
+                    *reinterpret_cast<uint32_t*>(dst) = packed;
                 }
             }
+            }
         }
-        // LDS operations of one wave complete in order: the reads see the writes
+        // LDS operations of one wave complete in order: the reads see the
+        // writes, and the next slice's writes follow these reads
+        uint4 v[NQ];
 #pragma unroll
-        for (int q = 0; q < 32 * CPR / 64; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int idx = lane + 64 * q;
-            const int rr = idx / CPR, ch = idx % CPR;
-            const uint4 v = *reinterpret_cast<const uint4*>(scratch + rr * PITCH + ch * 16);
-            const int grow = row0 + i * 32 + rr;
-            const int gcol = col0 + ch * EPC;
-            if (grow >= M) continue;
-            int8_t* out = static_cast<int8_t*>(Y) + (static_cast<int64_t>(grow) * N + gcol) * ES;
-            if (vec_ok && gcol + EPC <= N) {
-                *reinterpret_cast<uint4*>(out) = v;
-            } else {
-                const int8_t* src = reinterpret_cast<const int8_t*>(&v);
-                for (int e = 0; e < EPC; ++e)
-                    if (gcol + e < N)
-                        for (int b = 0; b < ES; ++b) out[e * ES + b] = src[e * ES + b];
+            v[q] = *reinterpret_cast<const uint4*>(scratch + (idx / CPR) * PITCH + (idx % CPR) * 16);
+        }
+        const int srow = row0 + i * 32;
+        if (cols_in && srow + 32 <= M) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int idx = lane + 64 * q;
+                int8_t* out = static_cast<int8_t*>(Y) +
+                              (static_cast<int64_t>(srow + idx / CPR) * N + col0 + (idx % CPR) * EPC) * ES;
+                *reinterpret_cast<uint4*>(out) = v[q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int idx = lane + 64 * q;
+                const int grow = srow + idx / CPR;
+                const int gcol = col0 + (idx % CPR) * EPC;
+                if (grow >= M) continue;
+                int8_t* out = static_cast<int8_t*>(Y) + (static_cast<int64_t>(grow) * N + gcol) * ES;
+#pragma unroll
+                for (int t = 0; t < EPC; ++t) {
+                    if (gcol + t >= N) continue;
+                    // element t of the chunk, taken from its 32-bit word by shift
+                    const int wi = t * ES / 4;
+                    const uint32_t wv = wi == 0 ? v[q].x : wi == 1 ? v[q].y : wi == 2 ? v[q].z : v[q].w;
+                    const uint32_t ev = wv >> (8 * ((t * ES) & 3));
+                    if (ES == 4) *reinterpret_cast<uint32_t*>(out + t * ES) = ev;
+                    else if (ES == 2) *reinterpret_cast<uint16_t*>(out + t * ES) = static_cast<uint16_t>(ev);
+                    else out[t] = static_cast<int8_t>(ev);
+                }
             }
         }
     }
@@ -632,10 +672,17 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
 
     __syncthreads();
     const int cw = wn * T::WN;
-    store_tile_t<OUT, T::TM, T::TN>(acc, m0 + wm * T::WM, n0 + cw, lane, scales + wm * T::WM,
-                                    scales + BM + cw, epi_cols + cw, epi_cols + BN + cw,
-                                    epi_cols + 2 * BN + cw, epi, D, rD, Y, M, N,
-                                    lds + wave * (32 * kEpiPitch));
+    int8_t* const scr = lds + wave * (32 * kEpiPitch);
+    if (epi.bias != nullptr || epi.relu)
+        store_tile_t<OUT, T::TM, T::TN, true>(acc, m0 + wm * T::WM, n0 + cw, lane,
+                                              scales + wm * T::WM, scales + BM + cw,
+                                              epi_cols + cw, epi_cols + BN + cw,
+                                              epi_cols + 2 * BN + cw, epi, D, rD, Y, M, N, scr);
+    else
+        store_tile_t<OUT, T::TM, T::TN, false>(acc, m0 + wm * T::WM, n0 + cw, lane,
+                                               scales + wm * T::WM, scales + BM + cw,
+                                               epi_cols + cw, epi_cols + BN + cw,
+                                               epi_cols + 2 * BN + cw, epi, D, rD, Y, M, N, scr);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
@@ -667,6 +714,170 @@ hipError_t run_pp(const int8_t* xq, const float* sx, bool per_token, const int8_
     return hipGetLastError();
 }
 
+// ---- short-K kernel (K = 64, 128 or 256, e.g. the attention scores Q K^T) ----
+//
+// With K this short a tile does little MFMA work per output byte, so the
+// kernel is bound by its output stores (and the operand loads of the next
+// tiles).  Each block loads the tile's whole K into LDS with one burst of
+// global_load_lds transfers (panels of 128- or 64-byte rows, swizzled as in
+// the ping-pong kernel), runs the MFMAs, and leaves through the transposed
+// 16-byte-store epilogue, whose scratch reuses the operand LDS.  Four waves
+// and at most 64 KB of LDS per block let several blocks share a CU, so one
+// block's stores overlap the loads and MFMAs of the others.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int KS, int OUT, bool FUSED>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
+__attribute__((amdgpu_waves_per_eu(KS == 256 ? 2 : OUT == kOutI8 ? (FUSED ? 2 : 3) : (FUSED ? 3 : 4))))
+void gemm_shortk_kernel(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
+    int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
+    int M, int N, int K, Epi epi, Batch bat) {
+    SQ_APPLY_BATCH(OUT);
+    using T = Tile<BM, BN, WAVES_M, WAVES_N>;
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int BKP = KS >= 128 ? 128 : 64;  // bytes per row of one LDS panel
+    constexpr int NP = KS / BKP;
+    constexpr int kRows = BM + BN;
+    constexpr int kPanel = kRows * BKP;
+    constexpr int kCPR = BKP / 16;
+    constexpr int kRowsPerXfer = 1024 / BKP;
+    constexpr int XPP = kRows / kRowsPerXfer;  // wave-wide transfers per panel
+    constexpr int IPW = XPP * NP / NW;         // transfers per wave
+    constexpr int NKK = BKP / 32;
+    static_assert(NP * BKP == KS && IPW * NW == XPP * NP, "panels divide over the waves");
+    static_assert(BM % kRowsPerXfer == 0, "a transfer never straddles A and B");
+    static_assert(IPW < 64, "vmcnt range");
+    constexpr int kEpiPitch = epi_pitch<OUT, T::TN>();
+    constexpr int kLds = NW * 32 * kEpiPitch > NP * kPanel ? NW * 32 * kEpiPitch : NP * kPanel;
+    static_assert(BM + BN <= 2 * T::kThreads && BN <= T::kThreads, "scale staging");
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kLds];
+    __shared__ __attribute__((aligned(16))) float scales[BM + BN];
+    __shared__ __attribute__((aligned(16))) float epi_cols[3 * BN];
+
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    int tmi, tni;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int st = threadIdx.x;
+
+    // scales and epilogue columns first (their loads retire before the
+    // transfers issued after them)
+    float sc0 = 0.0f, sc1 = 0.0f, cb = 0.0f, cs = 1.0f;
+    if (OUT != kOutI32) {
+        auto scale_of = [&](int r) {
+            return r < BM ? sx[sx_per_token ? min(m0 + r, M - 1) : 0]
+                          : sw[sw_per_tensor ? 0 : min(n0 + r - BM, N - 1)];
+        };
+        sc0 = scale_of(st);
+        if (st + T::kThreads < BM + BN) sc1 = scale_of(st + T::kThreads);
+        if (st < BN) {
+            const int col = min(n0 + st, N - 1);
+            if (epi.bias) cb = epi.bias[col];
+            if (OUT == kOutI8 && epi.next_s) cs = epi.next_s[col];
+        }
+    }
+    const float D = (OUT == kOutI8) ? *epi.next_step : 1.0f;
+    const float rD = 1.0f / D;
+    compiler_fence();
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int x = wave * IPW + i;
+        const int p = x / XPP, xi = x % XPP;
+        const int q = xi * 64 + lane;
+        const int row = q / kCPR;
+        const int c = (q % kCPR) ^ swz_k<BKP>(row);
+        const bool is_a = xi * kRowsPerXfer < BM;
+        const int off = is_a ? min(m0 + row, M - 1) * K : min(n0 + row - BM, N - 1) * K;
+        dma16(is_a ? A : B, static_cast<uint32_t>(off + p * BKP + c * 16),
+              lds_addr(lds + p * kPanel + xi * 1024));
+    }
+    wait_vmcnt<0>();
+    if (OUT != kOutI32) {
+        scales[st] = sc0;
+        if (st + T::kThreads < BM + BN) scales[st + T::kThreads] = sc1;
+        if (st < BN) {
+            epi_cols[st] = cb;
+            epi_cols[BN + st] = cs;
+            epi_cols[2 * BN + st] = 1.0f / cs;
+        }
+    }
+    compiler_fence();
+    __syncthreads();
+
+    v16i acc[T::TM][T::TN];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int8_t* S = lds + p * kPanel;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            v4i fa[T::TM], fb[T::TN];
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+                fa[i] = *reinterpret_cast<const v4i*>(
+                    S + lds_off_k<BKP>(wm * T::WM + i * 32 + frow, 2 * kk + fhalf));
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+                fb[j] = *reinterpret_cast<const v4i*>(
+                    S + BM * BKP + lds_off_k<BKP>(wn * T::WN + j * 32 + frow, 2 * kk + fhalf));
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j],
+                                                                      0, 0, 0);
+        }
+    }
+    __syncthreads();
+    const int cw = wn * T::WN;
+    // bias / ReLU chosen by the launch (one epilogue per kernel keeps the
+    // register count within four waves per SIMD)
+    store_tile_t<OUT, T::TM, T::TN, FUSED>(acc, m0 + wm * T::WM, n0 + cw, lane, scales + wm * T::WM,
+                                           scales + BM + cw, epi_cols + cw, epi_cols + BN + cw,
+                                           epi_cols + 2 * BN + cw, epi, D, rD, Y, M, N,
+                                           lds + wave * (32 * kEpiPitch));
+}
+
+template <int KS>
+hipError_t run_shortk(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
+                      const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out,
+                      const Epi& epi, const Batch& bat, hipStream_t stream) {
+    constexpr int BM = 128, BN = 128;
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const dim3 grid(tiles, static_cast<unsigned>(bat.count)), block(256);
+    const int pt = per_token ? 1 : 0;
+    const int wpt = w_per_tensor ? 1 : 0;
+    const bool fused = epi.bias != nullptr || epi.relu != 0;
+#define SQ_SK(OUT_, F_)                                                                      \
+    gemm_shortk_kernel<BM, BN, 2, 2, KS, OUT_, F_>                                           \
+        <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat)
+    switch (out) {
+        case kOutF32:
+            if (fused) SQ_SK(kOutF32, true); else SQ_SK(kOutF32, false);
+            break;
+        case kOutBF16:
+            if (fused) SQ_SK(kOutBF16, true); else SQ_SK(kOutBF16, false);
+            break;
+        case kOutI8:
+            if (fused) SQ_SK(kOutI8, true); else SQ_SK(kOutI8, false);
+            break;
+        default:  // int32 accumulators take no epilogue
+            SQ_SK(kOutI32, false);
+            break;
+    }
+#undef SQ_SK
+    return hipGetLastError();
+}
 
 // ---- skinny-M kernel (decode: M <= 64): streams W once from HBM ---------------
 //
@@ -844,6 +1055,18 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
             return launch_skinny(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, bat, stream);
         }
         return run<64, 128, 1, 4>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, bat, stream);
+    }
+    // short K: the whole K of a tile in LDS at once
+    if ((K == 64 || K == 128 || K == 256) && M * K < (int64_t(1) << 31) &&
+        N * K < (int64_t(1) << 31)) {
+        if (K == 64)
+            return run_shortk<64>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
+                                  out_kind, epi, bat, stream);
+        if (K == 128)
+            return run_shortk<128>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k,
+                                   y, out_kind, epi, bat, stream);
+        return run_shortk<256>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
+                               out_kind, epi, bat, stream);
     }
     // ping-pong kernels: K a multiple of the 128-byte stage of the 256x128
     // tile, operand offsets in int32
