@@ -326,11 +326,18 @@ def ref_smoothed_linear_f64(x, w, s) -> np.ndarray:
 
 # ---- whole-path composition (oracle side) ------------------------------------
 
-def calibrate(x_cal, w, alpha, gamma=None, beta=None, rows=None, w_per_tensor=False):
+def calibrate(x_cal, w, alpha, gamma=None, beta=None, rows=None, w_per_tensor=False,
+              act_stat=None):
     """Offline half: colmax of X_cal and W, eq. (4), smoothed int8 weights
     (per output channel, or per tensor for the [Review] §6.3 O1-O3 settings),
-    optional LayerNorm fold and the static activation scale."""
-    a = colmax(x_cal)
+    optional LayerNorm fold and the static activation scale.  act_stat [K]:
+    a per-channel activation statistic used in place of the calibration peak
+    (floored like the peak; [Teach] §四 allows a robust statistic), x_cal is
+    then not read."""
+    if act_stat is not None:
+        a = np.maximum(_f32(act_stat), FLOOR)
+    else:
+        a = colmax(x_cal)
     wm = colmax(w)
     s = smooth_factor(a, wm, alpha)
     if w_per_tensor:
@@ -390,3 +397,77 @@ def bmm_w8a8(xq, x_scale, wq, w_scale, per_token=True, w_per_tensor=False, out="
     outs = [gemm_w8a8(xq[b], x_scale[b], wq[b], w_scale[b], per_token=per_token, out=out,
                       w_per_tensor=w_per_tensor) for b in range(B)]
     return np.stack(outs)
+
+
+# ---- robust calibration ([Teach] §四, §六, §八) ---------------------------------
+
+def _as_f32(x) -> np.ndarray:
+    x = np.asarray(x)
+    return bf16_to_f32(x) if x.dtype == np.uint16 else np.ascontiguousarray(x, np.float32)
+
+
+def quantile_rank(T: int, q) -> int:
+    """1-based nearest rank of the q-quantile among T values: ceil(q T) in fp64,
+    at least 1 and at most T."""
+    import math
+    return max(1, min(int(T), math.ceil(float(np.float32(q)) * float(T))))
+
+
+def channel_quantile(x, q) -> np.ndarray:
+    """Robust per-channel activation statistic ([Teach] §四: the calibration may
+    record a robust statistic instead of the peak): for channel j the
+    nearest-rank q-quantile of |x[:, j]|, i.e. the quantile_rank(T, q)-th
+    smallest magnitude, floored at FLOOR.  q = 1 is the peak of a1."""
+    xa = np.abs(_as_f32(x))
+    T, K = xa.shape
+    if T == 0:
+        return np.full(K, FLOOR, np.float32)
+    v = np.sort(xa, axis=0)[quantile_rank(T, q) - 1]
+    return np.maximum(v, FLOOR).astype(np.float32)
+
+
+def clip_counts(xhat, scale):
+    """Saturation of the static quantizer ([Teach] §六: check the clip rate per
+    layer): codes whose rounded quotient rne(RN(xhat / scale)) lies outside
+    [-127, 127].  Returns (total, per-channel counts [K])."""
+    xh = _f32(xhat)
+    q = np.rint(xh / np.float32(scale))
+    c = np.abs(q) > 127
+    return int(c.sum()), c.sum(axis=0).astype(np.int64)
+
+
+def _rel(num: float, den: float) -> float:
+    return num / den if den > 0 else num
+
+
+def alpha_search(x_cal, w, alphas, mode="per_token", w_per_tensor=False):
+    """Candidate alphas for one linear ([Teach] §八: on candidate alphas measure
+    activation saturation, weight quantization error and the task set, per
+    layer if needed).  For each alpha, on the calibration batch:
+      err  = sum (y_q - y)^2 / sum y^2, y_q the dequantized fp32 output of the
+             quantized linear (activation mode as deployed), y = X W^T in fp64
+             (stands in for the task-set check, which needs a trained model);
+      werr = sum (W^ - dw q)^2 / sum W^^2 over the smoothed weights W^ = RN(W s)
+             and their dequantized codes (in fp64).
+    A ratio with a zero denominator is its numerator.  best = the first alpha
+    of least err.  The saturation check is clip_counts on held-out tokens."""
+    y64 = ref_linear_f64(x_cal, w)
+    den = float((y64 * y64).sum())
+    wf = _as_f32(w)
+    errs, werrs = [], []
+    for al in alphas:
+        cal = calibrate(x_cal, w, float(np.float32(al)), w_per_tensor=w_per_tensor)
+        static = cal["static_scale"] if mode == "static" else None
+        xq, xs, _ = smooth_quantize_act(x_cal, s=cal["s"], static=static,
+                                        dynamic_per_tensor=mode == "dynamic_per_tensor")
+        yq = gemm_w8a8(xq, xs, cal["wq"], cal["w_scale"], per_token=mode == "per_token",
+                       out="f32", w_per_tensor=w_per_tensor)
+        d = yq.astype(np.float64) - y64
+        errs.append(_rel(float((d * d).sum()), den))
+        what = (wf * cal["s"][None, :]).astype(np.float64)          # RN(W s) in fp32
+        ws = np.broadcast_to(cal["w_scale"].astype(np.float64)[:, None]
+                             if not w_per_tensor else cal["w_scale"].astype(np.float64)[0],
+                             what.shape)
+        dw = what - cal["wq"].astype(np.float64) * ws
+        werrs.append(_rel(float((dw * dw).sum()), float((what * what).sum())))
+    return np.array(errs), np.array(werrs), int(np.argmin(errs))

@@ -564,3 +564,142 @@ def test_int8_attention_scores_within_quantizer_bound():
         err = np.abs(s[h].astype(np.float64) - exact)
         assert np.all(err <= bound * (1 + 1e-6) + np.abs(exact) * 2.0 ** -22)
         assert np.array_equal(s[h], oracle.gemm_w8a8(qq[h], qs[h], kq[h], ks[h]))
+
+
+# ---- robust calibration ([Teach] §四, §六, §八) ------------------------------------
+
+def test_channel_quantile_is_the_inverted_cdf_quantile():
+    """Nearest rank equals numpy's inverted-CDF quantile (smallest value whose
+    empirical CDF reaches q) column by column.  q T is kept clear of integers
+    (the two rules may round such a product differently; the exact-integer
+    case is pinned in test_channel_quantile_extremes)."""
+    rng = np.random.default_rng(21)
+    for T in (1, 37, 513, 1001):
+        x = rng.standard_normal((T, 48)).astype(np.float32)
+        for q in (0.25, 0.5, 0.9, 0.999, 1.0):
+            qd = float(np.float32(q))
+            ref = np.quantile(np.abs(x), qd, axis=0, method="inverted_cdf")
+            got = oracle.channel_quantile(x, q)
+            assert np.array_equal(got, np.maximum(ref, oracle.FLOOR).astype(np.float32)), (T, q)
+
+
+def test_channel_quantile_order_statistic_with_ties():
+    """For rank r: fewer than r magnitudes lie below the result and at least r at
+    or below it (integer data with many ties; bf16 input bits)."""
+    import datagen
+    rng = np.random.default_rng(22)
+    x = rng.integers(-6, 7, size=(301, 40)).astype(np.float32)
+    xb = datagen.f32_to_bf16_bits(x)
+    for q in (0.01, 0.3, 0.5, 0.77, 1.0):
+        v = oracle.channel_quantile(xb, q)
+        r = oracle.quantile_rank(301, q)
+        a = np.abs(x)
+        below = (a < v[None, :]).sum(axis=0)
+        at_or_below = (a <= v[None, :]).sum(axis=0)
+        zero_col = v == oracle.FLOOR                   # a zero quantile is floored
+        assert np.all(below[~zero_col] < r) and np.all(at_or_below >= r)
+
+
+def test_channel_quantile_extremes():
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((64, 32)).astype(np.float32)
+    assert np.array_equal(oracle.channel_quantile(x, 1.0), oracle.colmax(x))   # the peak (a1)
+    mn = np.maximum(np.abs(x).min(axis=0), oracle.FLOOR)
+    assert np.array_equal(oracle.channel_quantile(x, 1e-9), mn)                  # rank 1
+    assert oracle.quantile_rank(64, 1e-9) == 1 and oracle.quantile_rank(64, 1.0) == 64
+    assert oracle.quantile_rank(10, 0.35) == 4 and oracle.quantile_rank(8, 0.5) == 4
+    assert np.all(oracle.channel_quantile(np.empty((0, 8), np.float32), 0.5) == oracle.FLOOR)
+
+
+def test_calibrate_from_peak_statistic_is_calibrate():
+    """A given statistic equal to the calibration peak reproduces the offline
+    half bit for bit, LayerNorm fold included; a lower robust statistic lowers
+    the static step, which then saturates the tokens above it."""
+    rng = np.random.default_rng(24)
+    xc = rng.standard_normal((128, 64)).astype(np.float32)
+    xc[:, 5] *= 40.0
+    w = (rng.standard_normal((48, 64)) * 0.05).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, 64).astype(np.float32)
+    b = (rng.standard_normal(64) * 0.1).astype(np.float32)
+    ref = oracle.calibrate(xc, w, 0.5, g, b)
+    got = oracle.calibrate(None, w, 0.5, g, b, act_stat=oracle.colmax(xc))
+    for k in ("a", "wmax", "s", "wq", "w_scale", "static_scale", "g_s", "b_s"):
+        assert np.array_equal(np.asarray(got[k]), np.asarray(ref[k])), k
+    rob = oracle.calibrate(None, w, 0.5, act_stat=oracle.channel_quantile(xc, 0.9))
+    assert rob["static_scale"] < ref["static_scale"]
+    xh = oracle.act_smooth(xc, rob["s"])
+    assert oracle.clip_counts(xh, rob["static_scale"])[0] > 0
+    xh0 = oracle.act_smooth(xc, ref["s"])
+    assert oracle.clip_counts(xh0, ref["static_scale"])[0] == 0      # the peak never clips
+
+
+def test_clip_counts_hand_example():
+    """Step 0.5 (x / step exact): 63.7 -> 127.4 -> 127 kept; 63.75 -> 127.5 -> 128
+    (tie to even) clipped; 63.25 -> 126.5 -> 126 kept; -63.75 clipped; 150 and
+    -64 clipped; 0 kept."""
+    xh = np.array([[63.7, 63.75, 63.25, -63.75],
+                   [150.0, -64.0, 0.0, 1.0]], np.float32)
+    total, per = oracle.clip_counts(xh, 0.5)
+    assert total == 4 and per.tolist() == [1, 2, 0, 1]
+    assert oracle.quant_static(xh, 0.5)[1] == total          # the C quantizer's own count
+
+
+def test_alpha_search_lossless_construction():
+    """Integer data whose column peaks m_j are the same for X and W (so s = 1
+    exactly at alpha = 0.5 and nowhere else) and whose every row attains 127:
+    at alpha = 0.5 every step is exactly 1 and the quantized linear is exact
+    (err = werr = 0), so 0.5 is chosen; other alphas smooth unevenly and lose."""
+    rng = np.random.default_rng(25)
+    T, K, N = 6, 16, 10
+    m = np.concatenate([np.full(4, 127), rng.integers(20, 127, size=K - 4)])
+    def grid(R):
+        a = np.stack([rng.integers(-mj, mj + 1, size=R) for mj in m], axis=1).astype(np.float32)
+        for j in range(K):
+            a[j % R, j] = m[j] if j % 2 else -m[j]          # each column attains m_j
+        for r in range(R):
+            a[r, r % 4] = 127.0                              # each row attains 127
+        return a
+    x, w = grid(T), grid(N)
+    assert np.array_equal(oracle.colmax(x), oracle.colmax(w))
+    alphas = [0.25, 0.5, 0.75]
+    for mode in ("per_token", "static", "dynamic_per_tensor"):
+        for wpt in (False, True):
+            err, werr, best = oracle.alpha_search(x, w, alphas, mode=mode, w_per_tensor=wpt)
+            assert err[1] == 0.0 and werr[1] == 0.0 and best == 1, (mode, wpt)
+            assert err[0] > 0 and err[2] > 0
+
+
+def test_alpha_search_hand_example():
+    """One token x = (1, 100), one output w = (1, 1), alpha = 0.5: s = (1, 10),
+    smoothed x and w both (1, 10), steps 10/127, codes (13, 127) on both sides,
+    y_q = 16298 * (10/127)^2 against y = 101; the weight error is
+    (1 - 13*10/127)^2 / (1 + 100).  Exact rationals; the fp32 steps and product
+    (about 3 ulp on y_q, i.e. 101 * 1.8e-7 against a difference of 0.048) move
+    err by at most 8e-4 relative, werr by far less."""
+    from fractions import Fraction as F
+    x = np.array([[1.0, 100.0]], np.float32)
+    w = np.array([[1.0, 1.0]], np.float32)
+    cal = oracle.calibrate(x, w, 0.5)
+    assert cal["s"].tolist() == [1.0, 10.0]
+    assert oracle.smooth_quantize_act(x, s=cal["s"])[0].tolist() == [[13, 127]]
+    assert cal["wq"].tolist() == [[13, 127]]
+    err, werr, best = oracle.alpha_search(x, w, [0.5])
+    d = F(10, 127)
+    e_exact = (F(16298) * d * d - 101) ** 2 / F(101) ** 2
+    w_exact = (1 - 13 * d) ** 2 / F(101)
+    assert abs(err[0] / float(e_exact) - 1) < 1e-3
+    assert abs(werr[0] / float(w_exact) - 1) < 1e-4 and best == 0
+
+
+def test_alpha_search_power_of_two_invariance():
+    """At alpha = 1 (s = a) and alpha = 0 (s = 1/w) doubling W scales every
+    intermediate by an exact power of two: both errors are unchanged bit for
+    bit, in every activation mode."""
+    rng = np.random.default_rng(26)
+    x = rng.standard_normal((40, 64)).astype(np.float32)
+    x[:, 3] *= 30.0
+    w = (rng.standard_normal((24, 64)) * 0.02).astype(np.float32)
+    for mode in ("per_token", "static", "dynamic_per_tensor"):
+        e1, w1, _ = oracle.alpha_search(x, w, [0.0, 1.0], mode=mode)
+        e2, w2, _ = oracle.alpha_search(x, 2 * w, [0.0, 1.0], mode=mode)
+        assert np.array_equal(e1, e2) and np.array_equal(w1, w2), mode
