@@ -60,6 +60,7 @@
 #ifndef SQ_H
 #define SQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -68,7 +69,7 @@ extern "C" {
 
 typedef struct ihipStream_t* sq_stream_t; /* a hipStream_t */
 
-#define SQ_ABI_VERSION 2
+#define SQ_ABI_VERSION 3
 #define SQ_MAX_K 133120          /* largest multiple of 64 with 127*127*K < 2^31 */
 #define SQ_ABSMAX_FLOOR 1e-7f    /* floor of every absolute maximum */
 
@@ -80,7 +81,8 @@ typedef enum {
     SQ_ERR_BAD_ALPHA = 4, /* alpha outside [0, 1] or not finite */
     SQ_ERR_ALIGNMENT = 5, /* pointer not 16-byte aligned */
     SQ_ERR_HIP = 6,       /* the HIP runtime rejected a launch */
-    SQ_ERR_BAD_MODE = 7   /* unknown mode, or a mode/argument combination */
+    SQ_ERR_BAD_MODE = 7,  /* unknown mode, or a mode/argument combination */
+    SQ_ERR_WORKSPACE = 8  /* workspace smaller than the size its query returns */
 } sq_status;
 
 typedef enum { SQ_F32 = 0, SQ_BF16 = 1, SQ_I8 = 2, SQ_I32 = 3 } sq_dtype;
@@ -245,6 +247,82 @@ sq_status sq_bmm_w8a8(const int8_t* xq, int64_t xq_stride, const float* x_scale,
                       int64_t wq_stride, const float* w_scale, int64_t ws_stride,
                       sq_weight_mode w_mode, int64_t batch, int64_t M, int64_t N, int64_t K,
                       void* y, int64_t y_stride, sq_dtype y_dt, sq_stream_t stream);
+
+/*
+ * Robust calibration ([Teach] §四: the calibration may record a robust
+ * per-channel statistic instead of the peak, and alpha is searched together
+ * with the weight range; §六: check the clip rate per layer and the stability
+ * of channel peaks so that no single sample dominates; §八: compare candidate
+ * alphas on activation saturation, weight quantization error and a task set).
+ *
+ * sq_channel_quantile -- for every channel j of x [T, K] (F32 or BF16) the
+ *   nearest-rank q-quantile of |x[:, j]|: the r-th smallest magnitude with
+ *   r = max(1, min(T, ceil(q * T))) computed in fp64, floored at
+ *   SQ_ABSMAX_FLOOR; q in (0, 1]; q = 1 is the peak of sq_calibrate.  T = 0
+ *   gives the floor.  out [K] fp32 (device).  workspace: device memory of at
+ *   least sq_channel_quantile_workspace_size(K) bytes, 16-byte aligned,
+ *   overwritten.  A radix select: ceil(bits / 8) passes over x (bits = 15 for
+ *   BF16, 31 for F32).  Channel-peak stability is the ratio of this call at
+ *   q = 1 to a lower q (a large ratio: few tokens set the peak).
+ */
+size_t sq_channel_quantile_workspace_size(int64_t K);
+sq_status sq_channel_quantile(const void* x, sq_dtype x_dt, int64_t T, int64_t K, float q,
+                              float* out, void* workspace, size_t workspace_bytes,
+                              sq_stream_t stream);
+
+/*
+ * sq_calibrate_stat -- sq_calibrate with a given per-channel activation
+ *   statistic act_stat [K] (device fp32, e.g. sq_channel_quantile) in place of
+ *   the calibration peak: a_j = max(SQ_ABSMAX_FLOOR, act_stat_j) enters
+ *   eq. (4) and the static step exactly as the peak does; a_out [K] receives
+ *   a_j.  Every other argument and output as in sq_calibrate.  A statistic
+ *   below the peak lowers the static step, which then saturates the tokens
+ *   above it (see sq_clip_count).
+ */
+sq_status sq_calibrate_stat(const float* act_stat, const void* w, sq_dtype w_dt, int64_t N,
+                            int64_t K, float alpha, sq_weight_mode w_mode,
+                            const float* ln_gamma, const float* ln_beta, float* s, int8_t* wq,
+                            float* w_scale, float* act_scale_static, float* ln_gamma_s,
+                            float* ln_beta_s, float* a_out, float* w_absmax,
+                            sq_stream_t stream);
+
+/*
+ * sq_clip_count -- the clip rate of the static quantizer on activations x
+ *   [M, K] (plain mode with s, or LayerNorm mode with ln_gamma_s / ln_beta_s,
+ *   as in sq_smooth_quantize_act) with the step static_scale [1] (device):
+ *   an element saturates when its rounded quotient rne(RN(x^ / dx_static))
+ *   lies outside [-127, 127].  count [1] (device) receives the number of
+ *   saturated elements; per_channel [K] (device, or NULL) the number per input
+ *   channel.  Both are overwritten; no codes are written.
+ */
+sq_status sq_clip_count(const void* x, sq_dtype x_dt, int64_t M, int64_t K, const float* s,
+                        const float* ln_gamma_s, const float* ln_beta_s, float ln_eps,
+                        const float* static_scale, unsigned long long* count,
+                        uint32_t* per_channel, sq_stream_t stream);
+
+/*
+ * sq_alpha_search -- candidate smoothing strengths for one linear layer.
+ *   x_cal [T, K] calibration activations (the layer's input), w [N, K], both
+ *   F32 or BF16 (device); alphas [n_alpha] (HOST array, each in [0, 1],
+ *   1 <= n_alpha <= 1024); x_mode / w_mode: the step granularities as
+ *   deployed.  For alpha_i the layer is calibrated (sq_calibrate), the
+ *   calibration tokens quantized (sq_smooth_quantize_act) and multiplied
+ *   (sq_gemm_w8a8, fp32 output y_q); then (device fp64 outputs)
+ *     err[i]  = sum (y_q - y)^2 / sum y^2,  y = X W^T computed in fp64
+ *     werr[i] = sum (W^ - dw q)^2 / sum W^^2 over W^ = RN(W s) and its codes
+ *   (a ratio with a zero denominator is its numerator; sums in a fixed order),
+ *   and best [1] (device int32) the first index of the least err.  err stands
+ *   in for the pages' task-set check; the saturation check is sq_clip_count
+ *   on held-out tokens with each candidate's static step.  workspace: at least
+ *   sq_alpha_search_workspace_size(T, N, K) bytes (about 12 T N + T K + N K),
+ *   16-byte aligned, overwritten.  Calls on one stream must not share it.
+ */
+size_t sq_alpha_search_workspace_size(int64_t T, int64_t N, int64_t K);
+sq_status sq_alpha_search(const void* x_cal, sq_dtype x_dt, int64_t T, const void* w,
+                          sq_dtype w_dt, int64_t N, int64_t K, const float* alphas, int n_alpha,
+                          sq_act_mode x_mode, sq_weight_mode w_mode, double* err, double* werr,
+                          int32_t* best, void* workspace, size_t workspace_bytes,
+                          sq_stream_t stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* sq_status_string(sq_status status);

@@ -45,6 +45,21 @@ def sample_idx(n: int, k: int, seed: int) -> np.ndarray:
     return np.sort(np.concatenate([[0, n - 1], mid])).astype(np.int64)
 
 
+_C5 = {}
+
+
+def c5_inputs():
+    """The LayerNorm pipeline workload (hidden 8192, 65536 calibration tokens),
+    generated once per process."""
+    if not _C5:
+        spec = datagen.workload(5).layers[0]
+        _C5["xc"] = datagen.calibration_x(spec)
+        _C5["w"] = datagen.weights(spec)
+        _C5["x"] = datagen.eval_x(spec)
+        _C5["gb"] = datagen.ln_params(spec)
+    return _C5
+
+
 def gpu_calibrate(x_cal, w, alpha, gamma=None, beta=None, w_mode="per_channel"):
     d = dev()
     xt, wt = to_dev(x_cal, d), to_dev(w, d)

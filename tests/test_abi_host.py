@@ -20,7 +20,7 @@ MIS = 0x1008    # 8-byte aligned only
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:sq_status|const char\s*\*|int)\s+(sq_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:sq_status|const char\s*\*|int|size_t)\s+(sq_\w+)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     L = sq.lib()
-    for code in range(8):
+    for code in range(9):
         s = L.sq_status_string(code).decode()
         assert s.startswith("SQ_")
     assert L.sq_status_string(99).decode() == "SQ_ERR_UNKNOWN"
@@ -221,3 +221,47 @@ def test_bmm_validation():
     assert _bmm(wqs=24) == 5
     assert _bmm(y=MIS) == 5
     assert _bmm(batch=0, xq=None, wq=None, y=None) == 0
+
+
+def test_robust_calibration_validation():
+    """Channel quantile, calibration from a statistic, clip count and alpha
+    search reject bad arguments (and a short workspace) before any device work."""
+    L = sq.lib()
+    nq = L.sq_channel_quantile_workspace_size(64)
+    assert nq >= 64 * 1024 and L.sq_channel_quantile_workspace_size(96) == 0
+
+    def q(x=P, dt=1, T=4, K=64, qq=0.5, out=P, ws=P, nb=nq):
+        return L.sq_channel_quantile(x, dt, T, K, qq, out, ws, nb, None)
+    assert q(qq=0.0) == 7 and q(qq=1.5) == 7 and q(qq=float("nan")) == 7
+    assert q(K=96) == 2 and q(T=-1) == 2 and q(dt=2) == 3
+    assert q(out=None) == 1 and q(ws=None) == 1 and q(x=None) == 1
+    assert q(x=MIS) == 5 and q(ws=MIS) == 5
+    assert q(nb=nq - 1) == 8
+
+    def cs(a=P, w=P, dt=1, N=4, K=64, alpha=0.5, wmode=0, g=None, b=None, s=P, wq=P, ws=P,
+           st=P, gs=None, bs=None, ao=P, wa=P):
+        return L.sq_calibrate_stat(a, w, dt, N, K, alpha, wmode, g, b, s, wq, ws, st, gs, bs, ao,
+                                   wa, None)
+    assert cs(a=None) == 1 and cs(ao=None) == 1 and cs(wq=None) == 1
+    assert cs(alpha=1.5) == 4 and cs(wmode=5) == 7 and cs(K=96) == 2 and cs(dt=3) == 3
+    assert cs(g=P) == 7 and cs(g=P, b=P) == 1 and cs(a=MIS) == 5
+
+    def c(x=P, dt=1, M=4, K=64, s=P, g=None, b=None, eps=1e-5, st=P, cnt=P, pc=None):
+        return L.sq_clip_count(x, dt, M, K, s, g, b, eps, st, cnt, pc, None)
+    assert c(st=None) == 1 and c(cnt=None) == 1 and c(s=None) == 1
+    assert c(g=P, b=P) == 7 and c(s=None, g=P) == 1 and c(s=None, g=P, b=P, eps=0.0) == 7
+    assert c(K=96) == 2 and c(dt=2) == 3 and c(pc=MIS) == 5 and c(cnt=MIS) == 5
+
+    na = L.sq_alpha_search_workspace_size(4, 4, 64)
+    assert na > 0 and L.sq_alpha_search_workspace_size(4, 4, 96) == 0
+    good = (ctypes.c_float * 2)(0.5, 0.25)
+    bad = (ctypes.c_float * 2)(0.5, 1.5)
+
+    def a(x=P, xdt=1, T=4, w=P, wdt=1, N=4, K=64, al=good, n=2, mode=0, wmode=0, err=P, werr=P,
+          best=P, ws=P, nb=na):
+        return L.sq_alpha_search(x, xdt, T, w, wdt, N, K, ctypes.addressof(al), n, mode, wmode,
+                                 err, werr, best, ws, nb, None)
+    assert a(n=0) == 2 and a(n=1025) == 2 and a(T=0) == 2 and a(K=96) == 2
+    assert a(al=bad) == 4 and a(mode=3) == 7 and a(wmode=2) == 7 and a(xdt=2) == 3
+    assert a(err=None) == 1 and a(best=None) == 1 and a(ws=None) == 1
+    assert a(err=MIS) == 5 and a(nb=na - 1) == 8

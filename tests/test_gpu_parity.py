@@ -18,7 +18,7 @@ import torch
 import datagen
 import oracle
 import w8a8_int8_gemm_colwise_amd as sq
-from sqcase import assert_same, dev, run_layer, say, to_dev, to_np
+from sqcase import assert_same, c5_inputs, dev, run_layer, say, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -121,24 +121,11 @@ def test_opt175b_layer_m4096(l):
     _full_size_properties(r, "per_token")
 
 
-_C5 = {}
-
-
-def _c5_inputs():
-    if not _C5:
-        spec = datagen.workload(5).layers[0]
-        _C5["xc"] = datagen.calibration_x(spec)
-        _C5["w"] = datagen.weights(spec)
-        _C5["x"] = datagen.eval_x(spec)
-        _C5["gb"] = datagen.ln_params(spec)
-    return _C5
-
-
 @pytest.mark.parametrize("mode", ["static", "per_token"])
 @pytest.mark.parametrize("alpha", datagen.ALPHA_SWEEP)
 def test_ln_pipeline_h8192_alpha_sweep(alpha, mode):
     spec = datagen.workload(5, alpha=alpha).layers[0]
-    d = _c5_inputs()
+    d = c5_inputs()
     g, b = d["gb"]
     r = run_layer(spec, d["xc"], d["w"], d["x"], mode, n_rows=16, n_cols=24, seed=int(alpha * 100),
                   out_kinds=("bf16",), gamma=g, beta=b, alpha=alpha)

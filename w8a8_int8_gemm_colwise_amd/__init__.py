@@ -11,6 +11,13 @@ functions carry the C ABI's names (include/sq.h):
   sq_smooth_quantize_act  runtime: X/s (or the folded LayerNorm), then
                           per-token or static per-tensor int8
   sq_gemm_w8a8            runtime: int8 GEMM, int32 accumulation, dequant
+  sq_gemm_w8a8_ex         the same with the fused epilogue (bias, ReLU, int8
+                          codes for the next linear)
+  sq_bmm_w8a8             batched int8 GEMM (the attention products)
+  sq_channel_quantile     robust per-channel activation statistic
+  sq_calibrate_stat       the offline half from a given activation statistic
+  sq_clip_count           saturation count of the static quantizer
+  sq_alpha_search         candidate alphas: output and weight errors
 
 There is no fallback: if libsq.so is missing or fails to load, every call
 raises.
@@ -29,7 +36,7 @@ SQ_F32, SQ_BF16, SQ_I8, SQ_I32 = 0, 1, 2, 3
 SQ_PER_TOKEN, SQ_STATIC_PER_TENSOR, SQ_DYNAMIC_PER_TENSOR = 0, 1, 2
 SQ_W_PER_CHANNEL, SQ_W_PER_TENSOR = 0, 1
 SQ_MAX_K = 133120
-SQ_ABI_VERSION = 2
+SQ_ABI_VERSION = 3
 
 # The SmoothQuant efficiency levels ([Review] §6.3): (weight mode, activation
 # mode).  "colwise" is the per-output-channel weight path with per-token
@@ -41,7 +48,9 @@ SETTINGS = {
     "O3": ("per_tensor", "static"),
 }
 EXPORTED = ("sq_calibrate", "sq_smooth_quantize_act", "sq_gemm_w8a8", "sq_gemm_w8a8_ex",
-            "sq_bmm_w8a8", "sq_status_string", "sq_abi_version")
+            "sq_bmm_w8a8", "sq_channel_quantile_workspace_size", "sq_channel_quantile",
+            "sq_calibrate_stat", "sq_clip_count", "sq_alpha_search_workspace_size",
+            "sq_alpha_search", "sq_status_string", "sq_abi_version")
 
 
 class SqEpilogue(ctypes.Structure):
@@ -80,6 +89,21 @@ def lib() -> ctypes.CDLL:
     L.sq_bmm_w8a8.restype = ci
     L.sq_bmm_w8a8.argtypes = [vp, i64, vp, i64, ci, vp, i64, vp, i64, ci, i64, i64, i64, i64,
                               vp, i64, ci, vp]
+    sz = ctypes.c_size_t
+    L.sq_channel_quantile_workspace_size.restype = sz
+    L.sq_channel_quantile_workspace_size.argtypes = [i64]
+    L.sq_channel_quantile.restype = ci
+    L.sq_channel_quantile.argtypes = [vp, ci, i64, i64, cf, vp, vp, sz, vp]
+    L.sq_calibrate_stat.restype = ci
+    L.sq_calibrate_stat.argtypes = [vp, vp, ci, i64, i64, cf, ci, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, vp, vp]
+    L.sq_clip_count.restype = ci
+    L.sq_clip_count.argtypes = [vp, ci, i64, i64, vp, vp, vp, cf, vp, vp, vp, vp]
+    L.sq_alpha_search_workspace_size.restype = sz
+    L.sq_alpha_search_workspace_size.argtypes = [i64, i64, i64]
+    L.sq_alpha_search.restype = ci
+    L.sq_alpha_search.argtypes = [vp, ci, i64, vp, ci, i64, i64, vp, ci, ci, ci, vp, vp, vp, vp,
+                                  sz, vp]
     L.sq_status_string.restype = ctypes.c_char_p
     L.sq_status_string.argtypes = [ci]
     L.sq_abi_version.restype = ci
@@ -279,3 +303,94 @@ def sq_bmm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor
         _ptr(wq), 0 if wq.dim() == 2 else N * K, _ptr(w_scale), _stride(w_scale, ws_n), wm,
         B, M, N, K, _ptr(y), M * N, code, _stream(xq.device)))
     return y
+
+
+# ---- robust calibration ---------------------------------------------------------
+
+def _workspace(nbytes: int, device, workspace=None) -> torch.Tensor:
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace must be a GPU tensor of at least {nbytes} bytes")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def sq_channel_quantile(x: torch.Tensor, q: float, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-channel nearest-rank q-quantile of |x[:, j]| (floored), fp32 [K]."""
+    _dev2d(x, "x")
+    T, K = x.shape
+    nb = lib().sq_channel_quantile_workspace_size(K)
+    ws = _workspace(nb, x.device, workspace)
+    if out is None:
+        out = torch.empty(K, dtype=torch.float32, device=x.device)
+    _check(lib().sq_channel_quantile(_ptr(x), _dt(x), T, K, float(q), _ptr(out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(x.device)))
+    return out
+
+
+def sq_calibrate_stat(act_stat: torch.Tensor, w: torch.Tensor, alpha: float,
+                      ln_gamma: torch.Tensor | None = None, ln_beta: torch.Tensor | None = None,
+                      out: dict | None = None, w_mode="per_channel") -> dict:
+    """sq_calibrate with a given activation statistic [K] in place of the peak:
+    returns dict(a, s, wq, w_scale, static_scale, w_absmax[, ln_gamma_s, ln_beta_s])."""
+    wm = _wmode(w_mode)
+    _dev2d(w, "w")
+    N, K = w.shape
+    if act_stat.dim() != 1 or act_stat.numel() != K or act_stat.dtype != torch.float32:
+        raise ValueError("act_stat must be a float32 [K] tensor")
+    dev = w.device
+    o = dict(out or {})
+    f32 = dict(dtype=torch.float32, device=dev)
+    o.setdefault("a", torch.empty(K, **f32))
+    o.setdefault("s", torch.empty(K, **f32))
+    o.setdefault("wq", torch.empty((N, K), dtype=torch.int8, device=dev))
+    o.setdefault("w_scale", torch.empty(N if wm == SQ_W_PER_CHANNEL else 1, **f32))
+    o.setdefault("static_scale", torch.empty(1, **f32))
+    o.setdefault("w_absmax", torch.empty(K, **f32))
+    if ln_gamma is not None:
+        o.setdefault("ln_gamma_s", torch.empty(K, **f32))
+        o.setdefault("ln_beta_s", torch.empty(K, **f32))
+    _check(lib().sq_calibrate_stat(
+        _ptr(act_stat), _ptr(w), _dt(w), N, K, float(alpha), wm, _ptr(ln_gamma), _ptr(ln_beta),
+        _ptr(o["s"]), _ptr(o["wq"]), _ptr(o["w_scale"]), _ptr(o["static_scale"]),
+        _ptr(o.get("ln_gamma_s")), _ptr(o.get("ln_beta_s")), _ptr(o["a"]), _ptr(o["w_absmax"]),
+        _stream(dev)))
+    return o
+
+
+def sq_clip_count(x: torch.Tensor, static_scale: torch.Tensor, s: torch.Tensor | None = None,
+                  ln_gamma_s: torch.Tensor | None = None, ln_beta_s: torch.Tensor | None = None,
+                  ln_eps: float = 1e-5, per_channel: bool = False):
+    """Saturated elements of the static quantizer: (count int64 [1], per-channel
+    int32 [K] or None)."""
+    _dev2d(x, "x")
+    M, K = x.shape
+    count = torch.empty(1, dtype=torch.int64, device=x.device)
+    pc = torch.empty(K, dtype=torch.int32, device=x.device) if per_channel else None
+    _check(lib().sq_clip_count(_ptr(x), _dt(x), M, K, _ptr(s), _ptr(ln_gamma_s), _ptr(ln_beta_s),
+                               float(ln_eps), _ptr(static_scale), _ptr(count), _ptr(pc),
+                               _stream(x.device)))
+    return count, pc
+
+
+def sq_alpha_search(x_cal: torch.Tensor, w: torch.Tensor, alphas, mode="per_token",
+                    w_mode="per_channel", workspace: torch.Tensor | None = None):
+    """Candidate alphas for one linear: (err fp64 [n], werr fp64 [n], best int32 [1])."""
+    _dev2d(x_cal, "x_cal")
+    _dev2d(w, "w")
+    T, K = x_cal.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError("x_cal and w disagree on K")
+    al = (ctypes.c_float * len(alphas))(*[float(a) for a in alphas])
+    nb = lib().sq_alpha_search_workspace_size(T, N, K)
+    ws = _workspace(nb, w.device, workspace)
+    err = torch.empty(len(alphas), dtype=torch.float64, device=w.device)
+    werr = torch.empty(len(alphas), dtype=torch.float64, device=w.device)
+    best = torch.empty(1, dtype=torch.int32, device=w.device)
+    _check(lib().sq_alpha_search(
+        _ptr(x_cal), _dt(x_cal), T, _ptr(w), _dt(w), N, K, ctypes.addressof(al), len(alphas),
+        _mode(mode), _wmode(w_mode), _ptr(err), _ptr(werr), _ptr(best), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(w.device)))
+    return err, werr, best

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "sq")
 LIB = os.path.join(HERE, "libsq.so")
-SOURCES = ["abi.hip", "calibrate.hip", "act_quant.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "calibrate.hip", "act_quant.hip", "gemm.hip", "robust.hip"]
 PROBE_LIB = os.path.join(HERE, "libsqprobe.so")
 PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"

@@ -2,6 +2,7 @@
 // See include/sq.h for the contract of every entry point.
 #include "../../include/sq.h"
 
+#include <algorithm>
 #include <cmath>
 
 #include "sq_internal.hpp"
@@ -47,7 +48,33 @@ sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T, const void* 
         x_cal, to_dt(x_dt), T, w, to_dt(w_dt), N, K, alpha, w_mode == SQ_W_PER_TENSOR, ln_gamma,
         ln_beta, s, wq, w_scale,
         act_scale_static, ln_gamma ? ln_gamma_s : nullptr, ln_gamma ? ln_beta_s : nullptr,
-        x_absmax, w_absmax, reinterpret_cast<hipStream_t>(stream)));
+        x_absmax, w_absmax, nullptr, reinterpret_cast<hipStream_t>(stream)));
+}
+
+sq_status sq_calibrate_stat(const float* act_stat, const void* w, sq_dtype w_dt, int64_t N,
+                            int64_t K, float alpha, sq_weight_mode w_mode,
+                            const float* ln_gamma, const float* ln_beta, float* s, int8_t* wq,
+                            float* w_scale, float* act_scale_static, float* ln_gamma_s,
+                            float* ln_beta_s, float* a_out, float* w_absmax,
+                            sq_stream_t stream) {
+    if (!valid_k(K) || !valid_rows(N)) return SQ_ERR_BAD_SHAPE;
+    if (!float_dtype(w_dt)) return SQ_ERR_BAD_DTYPE;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_BAD_ALPHA;
+    if (w_mode != SQ_W_PER_CHANNEL && w_mode != SQ_W_PER_TENSOR) return SQ_ERR_BAD_MODE;
+    if (!act_stat || !s || !a_out || !w_absmax) return SQ_ERR_NULL_ARG;
+    if (N > 0 && (!w || !wq)) return SQ_ERR_NULL_ARG;
+    if ((N > 0 || w_mode == SQ_W_PER_TENSOR) && !w_scale) return SQ_ERR_NULL_ARG;
+    if ((ln_gamma == nullptr) != (ln_beta == nullptr)) return SQ_ERR_BAD_MODE;
+    if (ln_gamma && (!ln_gamma_s || !ln_beta_s)) return SQ_ERR_NULL_ARG;
+    const void* ptrs[] = {act_stat, w, ln_gamma, ln_beta, s, wq, w_scale, act_scale_static,
+                          ln_gamma_s, ln_beta_s, a_out, w_absmax};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
+    return from_hip(sq::launch_calibrate(
+        nullptr, sq::Dt::F32, 0, w, to_dt(w_dt), N, K, alpha, w_mode == SQ_W_PER_TENSOR,
+        ln_gamma, ln_beta, s, wq, w_scale, act_scale_static, ln_gamma ? ln_gamma_s : nullptr,
+        ln_gamma ? ln_beta_s : nullptr, a_out, w_absmax, act_stat,
+        reinterpret_cast<hipStream_t>(stream)));
 }
 
 sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
@@ -162,6 +189,84 @@ sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_mode x_mod
                            stream);
 }
 
+size_t sq_channel_quantile_workspace_size(int64_t K) {
+    return valid_k(K) ? sq::quantile_workspace_bytes(K) : 0;
+}
+
+sq_status sq_channel_quantile(const void* x, sq_dtype x_dt, int64_t T, int64_t K, float q,
+                              float* out, void* workspace, size_t workspace_bytes,
+                              sq_stream_t stream) {
+    if (!valid_k(K) || !valid_rows(T)) return SQ_ERR_BAD_SHAPE;
+    if (!float_dtype(x_dt)) return SQ_ERR_BAD_DTYPE;
+    if (!(q > 0.0f && q <= 1.0f)) return SQ_ERR_BAD_MODE;
+    if (!out || !workspace || (T > 0 && !x)) return SQ_ERR_NULL_ARG;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return SQ_ERR_ALIGNMENT;
+    if (workspace_bytes < sq::quantile_workspace_bytes(K)) return SQ_ERR_WORKSPACE;
+    const int64_t r = std::max<int64_t>(
+        1, std::min<int64_t>(T, static_cast<int64_t>(std::ceil(static_cast<double>(q) *
+                                                               static_cast<double>(T)))));
+    return from_hip(sq::launch_channel_quantile(x, to_dt(x_dt), T, K, r, out, workspace,
+                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+sq_status sq_clip_count(const void* x, sq_dtype x_dt, int64_t M, int64_t K, const float* s,
+                        const float* ln_gamma_s, const float* ln_beta_s, float ln_eps,
+                        const float* static_scale, unsigned long long* count,
+                        uint32_t* per_channel, sq_stream_t stream) {
+    if (!valid_k(K) || !valid_rows(M)) return SQ_ERR_BAD_SHAPE;
+    if (!float_dtype(x_dt)) return SQ_ERR_BAD_DTYPE;
+    const bool ln = (ln_gamma_s != nullptr) || (ln_beta_s != nullptr);
+    if (ln) {
+        if (s) return SQ_ERR_BAD_MODE;
+        if (!ln_gamma_s || !ln_beta_s) return SQ_ERR_NULL_ARG;
+        if (!(ln_eps > 0.0f) || !std::isfinite(ln_eps)) return SQ_ERR_BAD_MODE;
+    } else if (!s) {
+        return SQ_ERR_NULL_ARG;
+    }
+    if (!static_scale || !count || (M > 0 && !x)) return SQ_ERR_NULL_ARG;
+    const void* ptrs[] = {x, s, ln_gamma_s, ln_beta_s, static_scale, count, per_channel};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
+    return from_hip(sq::launch_clip_count(x, to_dt(x_dt), M, K, ln ? nullptr : s, ln_gamma_s,
+                                          ln_beta_s, ln_eps, static_scale, count, per_channel,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t sq_alpha_search_workspace_size(int64_t T, int64_t N, int64_t K) {
+    if (!valid_k(K) || !valid_rows(T) || !valid_rows(N)) return 0;
+    return sq::alpha_workspace_bytes(T, N, K);
+}
+
+sq_status sq_alpha_search(const void* x_cal, sq_dtype x_dt, int64_t T, const void* w,
+                          sq_dtype w_dt, int64_t N, int64_t K, const float* alphas, int n_alpha,
+                          sq_act_mode x_mode, sq_weight_mode w_mode, double* err, double* werr,
+                          int32_t* best, void* workspace, size_t workspace_bytes,
+                          sq_stream_t stream) {
+    if (!valid_k(K) || !valid_rows(T) || !valid_rows(N) || T < 1 || N < 1)
+        return SQ_ERR_BAD_SHAPE;
+    if (T * N > (int64_t(1) << 31)) return SQ_ERR_BAD_SHAPE;
+    if (!float_dtype(x_dt) || !float_dtype(w_dt)) return SQ_ERR_BAD_DTYPE;
+    if (x_mode != SQ_PER_TOKEN && x_mode != SQ_STATIC_PER_TENSOR &&
+        x_mode != SQ_DYNAMIC_PER_TENSOR)
+        return SQ_ERR_BAD_MODE;
+    if (w_mode != SQ_W_PER_CHANNEL && w_mode != SQ_W_PER_TENSOR) return SQ_ERR_BAD_MODE;
+    if (n_alpha < 1 || n_alpha > 1024) return SQ_ERR_BAD_SHAPE;
+    if (!x_cal || !w || !alphas || !err || !werr || !best || !workspace) return SQ_ERR_NULL_ARG;
+    for (int i = 0; i < n_alpha; ++i)
+        if (!(alphas[i] >= 0.0f && alphas[i] <= 1.0f)) return SQ_ERR_BAD_ALPHA;
+    const void* ptrs[] = {x_cal, w, err, werr, best, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return SQ_ERR_ALIGNMENT;
+    if (workspace_bytes < sq::alpha_workspace_bytes(T, N, K)) return SQ_ERR_WORKSPACE;
+    const sq::ActMode am = x_mode == SQ_PER_TOKEN           ? sq::ActMode::PerToken
+                           : x_mode == SQ_STATIC_PER_TENSOR ? sq::ActMode::Static
+                                                            : sq::ActMode::DynamicTensor;
+    return from_hip(sq::launch_alpha_search(x_cal, to_dt(x_dt), T, w, to_dt(w_dt), N, K, alphas,
+                                            n_alpha, am, w_mode == SQ_W_PER_TENSOR, err, werr,
+                                            best, workspace,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 const char* sq_status_string(sq_status status) {
     switch (status) {
         case SQ_OK: return "SQ_OK";
@@ -172,6 +277,7 @@ const char* sq_status_string(sq_status status) {
         case SQ_ERR_ALIGNMENT: return "SQ_ERR_ALIGNMENT: pointers must be 16-byte aligned";
         case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime rejected a kernel launch";
         case SQ_ERR_BAD_MODE: return "SQ_ERR_BAD_MODE: invalid mode or mode/argument combination";
+        case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace smaller than its size query";
     }
     return "SQ_ERR_UNKNOWN";
 }

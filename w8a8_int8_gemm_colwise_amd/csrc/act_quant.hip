@@ -75,12 +75,41 @@ __device__ __forceinline__ int quantize(float xh, float d, float rd) {
     return code_of(div_rn(xh, d, rd));
 }
 
+// Whether the static quantizer saturates xh: its rounded quotient (after the
+// same dividend limit as quantize) lies outside [-127, 127].
+__device__ __forceinline__ bool saturates(float xh, float d, float rd) {
+    const float lim = 128.0f * d;
+    xh = fminf(fmaxf(xh, -lim), lim);
+    return fabsf(__builtin_rintf(div_rn(xh, d, rd))) > kQmax;
+}
+
+// Count mode of the static kernels (clip != nullptr): element k of a row
+// that saturates adds 1 to clip_ch[k] (if given) and to the lane's count; the
+// counts of a wave are summed and added to *clip once at the end.
+__device__ __forceinline__ void count_clips(const float (&v)[kChunk], float d, float rd,
+                                            int64_t c, uint32_t* clip_ch, int& n) {
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) {
+        if (saturates(v[e], d, rd)) {
+            ++n;
+            if (clip_ch) atomicAdd(clip_ch + c * kChunk + e, 1u);
+        }
+    }
+}
+
+__device__ __forceinline__ void flush_clips(int n, unsigned long long* clip) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o, 64);
+    if ((threadIdx.x & 63) == 0 && n > 0) atomicAdd(clip, static_cast<unsigned long long>(n));
+}
+
 // D > 0: the lane's per-column constants (s_k and RN(1/s_k) in plain mode,
 // gamma'_k and beta'_k in LayerNorm mode) are loaded once per block and kept in
 // registers, and the loads of the block's next D rows are in flight while the
 // current row is reduced and quantized (a ring of D+1 rows of 16-byte chunks).
 // D = 0: the constants are re-read per row (L2 hits), 1/s_k is an IEEE
 // division, and nothing is prefetched.
+// clip != nullptr (static mode only): count mode, see count_clips; no codes.
 // rowmax != nullptr (dynamic modes only): the row pass that stores the raw
 // maximum max_k |xh_k| of every row in rowmax[m] and writes neither codes nor
 // x_scale -- the first pass of the dynamic per-tensor step.
@@ -89,7 +118,8 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
     const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
     const float* __restrict__ gs, const float* __restrict__ bs, float eps,
     const float* __restrict__ static_scale, int8_t* __restrict__ xq,
-    float* __restrict__ x_scale, float* __restrict__ rowmax) {
+    float* __restrict__ x_scale, float* __restrict__ rowmax, unsigned long long* __restrict__ clip,
+    uint32_t* __restrict__ clip_ch) {
     __shared__ float lds[kLnThreads + 4];
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
@@ -136,6 +166,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
         d_static = *static_scale;
         rd_static = 1.0f / d_static;
     }
+    int nclip = 0;
     for (int64_t m = blockIdx.x; m < M; m += G) {
         if (m + D * G < M) fetch(m + D * G, ring[D]);
         float v[CPT][kChunk];
@@ -234,7 +265,13 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
                 else x_scale[m] = d;
             }
         }
-        if (STATIC || rowmax == nullptr) {
+        if (STATIC && clip) {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+                if (c < chunks) count_clips(v[i], d, rd, c, clip_ch, nclip);
+            }
+        } else if (STATIC || rowmax == nullptr) {
             int8_t* orow = xq + m * K;
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
@@ -252,6 +289,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
 #pragma unroll
             for (int i = 0; i < CPT; ++i) ring[j][i] = ring[j + 1][i];
     }
+    if (STATIC && clip) flush_clips(nclip, clip);
 }
 
 // Short rows (plain mode, K <= 256: at most 32 chunks).  A wave quantizes
@@ -264,7 +302,8 @@ template <typename T, bool STATIC, int SG>
 __global__ __launch_bounds__(256) void act_quant_rows_kernel(
     const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
     const float* __restrict__ static_scale, int8_t* __restrict__ xq,
-    float* __restrict__ x_scale, float* __restrict__ rowmax) {
+    float* __restrict__ x_scale, float* __restrict__ rowmax, unsigned long long* __restrict__ clip,
+    uint32_t* __restrict__ clip_ch) {
     constexpr int R = 64 / SG;
     const int lane = threadIdx.x & 63;
     const int r = lane / SG, c = lane % SG;
@@ -294,6 +333,7 @@ __global__ __launch_bounds__(256) void act_quant_rows_kernel(
         d_static = *static_scale;
         rd_static = 1.0f / d_static;
     }
+    int nclip = 0;
     for (; g < groups; g += W) {
         if (g + W < groups) fetch(g + W, nxt);
         const int64_t m = g * R + r;
@@ -321,7 +361,9 @@ __global__ __launch_bounds__(256) void act_quant_rows_kernel(
                 else x_scale[m] = d;
             }
         }
-        if ((STATIC || rowmax == nullptr) && live) {
+        if (STATIC && clip) {
+            if (live) count_clips(v, d, rd, c, clip_ch, nclip);
+        } else if ((STATIC || rowmax == nullptr) && live) {
             int q[kChunk];
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[e], d, rd);
@@ -329,6 +371,7 @@ __global__ __launch_bounds__(256) void act_quant_rows_kernel(
         }
         cur = nxt;
     }
+    if (STATIC && clip) flush_clips(nclip, clip);
 }
 
 // Any K: the row is re-read from memory for each sweep (mostly L2 hits).
@@ -362,11 +405,13 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_stream_kernel(
     const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
     const float* __restrict__ gs, const float* __restrict__ bs, float eps,
     const float* __restrict__ static_scale, int8_t* __restrict__ xq,
-    float* __restrict__ x_scale, float* __restrict__ rowmax) {
+    float* __restrict__ x_scale, float* __restrict__ rowmax, unsigned long long* __restrict__ clip,
+    uint32_t* __restrict__ clip_ch) {
     __shared__ float lds[kLnThreads + 4];
     const int tid = threadIdx.x;
     const int64_t chunks = K / kChunk;
     const float kf = static_cast<float>(K);
+    int nclip = 0;
     for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
         const T* row = x + m * K;
         float mu = 0.0f, rho = 0.0f;
@@ -416,12 +461,17 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_stream_kernel(
         for (int64_t c = tid; c < chunks; c += kLnThreads) {
             float v[kChunk];
             smooth_chunk<T, LN>(row, c, s, gs, bs, mu, rho, v);
+            if (STATIC && clip) {
+                count_clips(v, d, rd, c, clip_ch, nclip);
+                continue;
+            }
             int q[kChunk];
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[e], d, rd);
             *reinterpret_cast<uint2*>(xq + m * K + c * kChunk) = pack8(q);
         }
     }
+    if (STATIC && clip) flush_clips(nclip, clip);
 }
 
 struct ActArgs {
@@ -433,6 +483,8 @@ struct ActArgs {
     int8_t* xq;
     float* x_scale;
     float* rowmax;  // non-null: row-maximum pass (dynamic per-tensor step)
+    unsigned long long* clip = nullptr;  // non-null: count mode of the static quantizer
+    uint32_t* clip_ch = nullptr;         // per-channel counts in count mode (optional)
 };
 
 template <typename T, bool LN, bool STATIC, int CPT, int D, int MAXT = 1024>
@@ -442,7 +494,7 @@ hipError_t run(const ActArgs& a, int threads, hipStream_t stream) {
     const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.M, 256 * per_cu));
     act_quant_kernel<T, LN, STATIC, CPT, D, MAXT><<<grid, threads, 0, stream>>>(
         static_cast<const T*>(a.x), a.M, a.K, a.s, a.gs, a.bs, a.eps, a.static_scale, a.xq,
-        a.x_scale, a.rowmax);
+        a.x_scale, a.rowmax, a.clip, a.clip_ch);
     return hipGetLastError();
 }
 
@@ -451,7 +503,7 @@ hipError_t run_stream(const ActArgs& a, hipStream_t stream) {
     const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.M, 2048));
     act_quant_stream_kernel<T, LN, STATIC><<<grid, kLnThreads, 0, stream>>>(
         static_cast<const T*>(a.x), a.M, a.K, a.s, a.gs, a.bs, a.eps, a.static_scale, a.xq,
-        a.x_scale, a.rowmax);
+        a.x_scale, a.rowmax, a.clip, a.clip_ch);
     return hipGetLastError();
 }
 
@@ -463,7 +515,8 @@ hipError_t run_rows(const ActArgs& a, hipStream_t stream) {
     const int64_t groups = (a.M + 64 / SG - 1) / (64 / SG);
     const unsigned grid = static_cast<unsigned>(std::min<int64_t>((groups + 3) / 4, 256 * 8));
     act_quant_rows_kernel<T, STATIC, SG><<<grid, 256, 0, stream>>>(
-        static_cast<const T*>(a.x), a.M, a.K, a.s, a.static_scale, a.xq, a.x_scale, a.rowmax);
+        static_cast<const T*>(a.x), a.M, a.K, a.s, a.static_scale, a.xq, a.x_scale, a.rowmax,
+        a.clip, a.clip_ch);
     return hipGetLastError();
 }
 
@@ -498,6 +551,19 @@ hipError_t dispatch_ln(const ActArgs& a, hipStream_t stream) {
     return run_stream<T, true, STATIC>(a, stream);
 }
 
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        p[i] = 0u;
+}
+
+hipError_t zero_words(uint32_t* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 1024));
+    zero_words_kernel<<<grid, 256, 0, stream>>>(p, n);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t dispatch(const ActArgs& a, bool ln, bool st, hipStream_t stream) {
     if (ln) return st ? dispatch_ln<T, true>(a, stream) : dispatch_ln<T, false>(a, stream);
@@ -505,6 +571,20 @@ hipError_t dispatch(const ActArgs& a, bool ln, bool st, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_clip_count(const void* x, Dt x_dt, int64_t M, int64_t K, const float* s,
+                             const float* gamma_s, const float* beta_s, float eps,
+                             const float* static_scale, unsigned long long* clip,
+                             uint32_t* clip_ch, hipStream_t stream) {
+    hipError_t e = zero_words(reinterpret_cast<uint32_t*>(clip), 2, stream);
+    if (e == hipSuccess && clip_ch) e = zero_words(clip_ch, K, stream);
+    if (e != hipSuccess || M <= 0) return e;
+    const bool ln = (s == nullptr);
+    ActArgs a{x, M, K, s, gamma_s, beta_s, eps, static_scale, nullptr, nullptr, nullptr, clip,
+              clip_ch};
+    return (x_dt == Dt::BF16) ? dispatch<uint16_t>(a, ln, true, stream)
+                              : dispatch<float>(a, ln, true, stream);
+}
 
 hipError_t launch_act_quant(const void* x, Dt x_dt, int64_t M, int64_t K, const float* s,
                             const float* gamma_s, const float* beta_s, float eps,

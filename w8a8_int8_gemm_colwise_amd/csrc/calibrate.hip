@@ -219,7 +219,8 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
     float* __restrict__ a, float* __restrict__ w, int64_t K, float alpha,
     const uint32_t* __restrict__ partial, int splits_x, int splits_w,
     const float* __restrict__ gamma, const float* __restrict__ beta, float* __restrict__ s,
-    float* __restrict__ gamma_s, float* __restrict__ beta_s, uint32_t* __restrict__ static_bits) {
+    float* __restrict__ gamma_s, float* __restrict__ beta_s, uint32_t* __restrict__ static_bits,
+    const float* __restrict__ act_stat) {
     __shared__ float red[kFactorThreads / 64];
     const double al = static_cast<double>(alpha);
     const double be = 1.0 - al;
@@ -250,6 +251,11 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
         } else {
             aj = a[j];
             wj = w[j];
+        }
+        if (act_stat) {
+            // a given per-channel activation statistic replaces the peak
+            aj = fmaxf(act_stat[j], kFloor);
+            a[j] = aj;
         }
         // eq. (4) in fp64, rounded once to fp32
         const float sj = static_cast<float>(pow(static_cast<double>(aj), al) /
@@ -531,7 +537,9 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
                             int64_t N, int64_t K, float alpha, bool w_per_tensor, const float* gamma,
                             const float* beta, float* s, int8_t* wq, float* w_scale,
                             float* act_scale_static, float* gamma_s, float* beta_s,
-                            float* x_absmax, float* w_absmax, hipStream_t stream) {
+                            float* x_absmax, float* w_absmax, const float* act_stat,
+                            hipStream_t stream) {
+    if (act_stat) T = 0;  // the calibration activations are not read
     uint32_t* xa = reinterpret_cast<uint32_t*>(x_absmax);
     uint32_t* wa = reinterpret_cast<uint32_t*>(w_absmax);
     uint32_t* sb = reinterpret_cast<uint32_t*>(act_scale_static);
@@ -571,7 +579,7 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
     const int64_t fgrid = std::min<int64_t>((K + kFactorThreads - 1) / kFactorThreads, 1024);
     smooth_factor_kernel<<<static_cast<unsigned>(fgrid), kFactorThreads, 0, stream>>>(
         x_absmax, w_absmax, K, alpha, partial, px.splits, pw.splits, gamma, beta, s, gamma_s,
-        beta_s, sb);
+        beta_s, sb, act_stat);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 

@@ -1,0 +1,445 @@
+// robust.hip -- calibration robustness: a robust per-channel activation
+// statistic, and the search over candidate smoothing strengths alpha.
+//
+//   [Teach] "SmoothQuant 如何解决激活量化难题？为什么适合 W8A8？"
+//   §四: the calibration records per-channel activation peaks or a robust
+//   statistic, and alpha / s is searched together with the weight range;
+//   §六: the clip rate per layer and the stability of channel peaks are to be
+//   checked, so that no single sample dominates the scales; §八: candidate
+//   alphas are compared on activation saturation, weight quantization error
+//   and a task set, per layer if needed.
+//
+// Channel quantile.  The nearest-rank q-quantile of |x[:, j]| is found by a
+// radix select on the magnitude bit pattern (non-negative floats order like
+// their bit patterns): 15 bits for bf16, 31 for fp32, 8 bits per pass.  Each
+// pass counts, per column, the elements whose higher bits equal the prefix
+// chosen so far, in a histogram of the next digit (LDS per block, then added
+// into a global [K][256] histogram); a per-column select step walks that
+// histogram to the bin holding the remaining rank and extends the prefix.
+//
+// Alpha search.  The fp64 product Y = X W^T of the calibration tokens is the
+// reference; for each alpha the existing launchers calibrate, quantize the
+// calibration tokens as deployed and run the int8 GEMM with fp32 output;
+// deterministic two-level fp64 reductions give sum (y_q - y)^2 / sum y^2 and
+// the weight quantization error sum (W^ - dw q)^2 / sum W^^2, W^ = RN(W s).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "sq_device.hpp"
+#include "sq_internal.hpp"
+
+namespace sq {
+namespace {
+
+// ---- channel quantile -------------------------------------------------------
+
+template <typename T> struct Mag;
+template <> struct Mag<uint16_t> {
+    static constexpr int kBits = 15;
+    __device__ static uint32_t of(uint16_t v) { return v & 0x7fffu; }
+    __device__ static float value(uint32_t m) { return __uint_as_float(m << 16); }
+};
+template <> struct Mag<float> {
+    static constexpr int kBits = 31;
+    __device__ static uint32_t of(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+    __device__ static float value(uint32_t m) { return __uint_as_float(m); }
+};
+
+constexpr int kQCols = 64;       // columns per block, one per lane
+constexpr int kQThreads = 512;   // 8 waves walk interleaved rows
+constexpr int kQBins = 256;
+constexpr int kQPitch = 257;     // padded LDS row: equal bins of different columns in different banks
+constexpr int kQUnroll = 4;
+
+template <typename T>
+__global__ __launch_bounds__(kQThreads) void quantile_hist_kernel(
+    const T* __restrict__ x, int64_t rows, int64_t K, int64_t rpb, int shift, int width,
+    const uint32_t* __restrict__ prefix, uint32_t* __restrict__ hist) {
+    __shared__ uint32_t h[kQCols * kQPitch];
+    for (int i = threadIdx.x; i < kQCols * kQPitch; i += kQThreads) h[i] = 0u;
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * kQCols + lane;
+    const int hi = shift + width;   // at most 31: magnitude bits above the digit
+    const uint32_t mask = (1u << width) - 1u;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rpb;
+    const int64_t r1 = std::min<int64_t>(rows, r0 + rpb);
+    if (col < K) {
+        const uint32_t pre = prefix[col];
+        uint32_t* hl = h + lane * kQPitch;
+        constexpr int kStride = kQThreads / 64;
+        int64_t t = r0 + wave;
+        for (; t + (kQUnroll - 1) * kStride < r1; t += kQUnroll * kStride) {
+            T v[kQUnroll];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) v[u] = x[(t + u * kStride) * K + col];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u) {
+                const uint32_t m = Mag<T>::of(v[u]);
+                if ((m >> hi) == pre) atomicAdd(hl + ((m >> shift) & mask), 1u);
+            }
+        }
+        for (; t < r1; t += kStride) {
+            const uint32_t m = Mag<T>::of(x[t * K + col]);
+            if ((m >> hi) == pre) atomicAdd(hl + ((m >> shift) & mask), 1u);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kQCols * kQBins; i += kQThreads) {
+        const int c = i / kQBins, b = i % kQBins;
+        const int64_t gc = static_cast<int64_t>(blockIdx.x) * kQCols + c;
+        const uint32_t n = h[c * kQPitch + b];
+        if (gc < K && n) atomicAdd(hist + gc * kQBins + b, n);
+    }
+}
+
+// One thread per column: the bin of the digit that holds the remaining rank
+// extends the prefix; the histogram row is cleared for the next pass.  After
+// the last pass the prefix is the whole magnitude pattern of the quantile.
+template <typename T>
+__global__ __launch_bounds__(256) void quantile_select_kernel(
+    int64_t K, int width, uint32_t* __restrict__ prefix, uint32_t* __restrict__ rank,
+    uint32_t* __restrict__ hist, float* __restrict__ out, int last) {
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (col >= K) return;
+    uint32_t* hc = hist + col * kQBins;
+    const uint32_t r = rank[col];
+    const int nb = 1 << width;
+    uint32_t cum = 0u;
+    int b = 0;
+    for (; b < nb - 1; ++b) {
+        const uint32_t c = hc[b];
+        if (cum + c >= r) break;
+        cum += c;
+    }
+    for (int i = 0; i < nb; ++i) hc[i] = 0u;
+    const uint32_t p = (prefix[col] << width) | static_cast<uint32_t>(b);
+    prefix[col] = p;
+    rank[col] = r - cum;
+    if (last) out[col] = fmaxf(Mag<T>::value(p), kFloor);
+}
+
+__global__ __launch_bounds__(256) void quantile_init_kernel(int64_t K, uint32_t rank0,
+                                                            uint32_t* __restrict__ prefix,
+                                                            uint32_t* __restrict__ rank,
+                                                            uint32_t* __restrict__ hist,
+                                                            float* __restrict__ out, int empty) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < K * kQBins;
+         i += stride) {
+        hist[i] = 0u;
+        if (i < K) {
+            prefix[i] = 0u;
+            rank[i] = rank0;
+            if (empty) out[i] = kFloor;
+        }
+    }
+}
+
+template <typename T>
+hipError_t run_quantile(const T* x, int64_t rows, int64_t K, int64_t rank0, float* out,
+                        uint32_t* hist, uint32_t* prefix, uint32_t* rank, hipStream_t stream) {
+    const unsigned igrid = static_cast<unsigned>(std::min<int64_t>((K * kQBins + 255) / 256, 2048));
+    quantile_init_kernel<<<igrid, 256, 0, stream>>>(K, static_cast<uint32_t>(rank0), prefix, rank,
+                                                    hist, out, rows == 0 ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || rows == 0) return e;
+    // about two blocks per CU over the strips of 64 columns
+    const int64_t strips = (K + kQCols - 1) / kQCols;
+    const int64_t want = std::max<int64_t>(1, (512 + strips - 1) / strips);
+    const int64_t splits = std::min<int64_t>({want, (rows + 255) / 256, 65535});
+    const int64_t rpb = (rows + splits - 1) / splits;
+    const dim3 hgrid(static_cast<unsigned>(strips), static_cast<unsigned>((rows + rpb - 1) / rpb));
+    const unsigned sgrid = static_cast<unsigned>((K + 255) / 256);
+    constexpr int NB = Mag<T>::kBits;
+    const int passes = (NB + 7) / 8;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = std::max(0, NB - 8 * (p + 1));
+        const int width = NB - 8 * p - shift;
+        quantile_hist_kernel<T><<<hgrid, kQThreads, 0, stream>>>(x, rows, K, rpb, shift, width,
+                                                                  prefix, hist);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        quantile_select_kernel<T><<<sgrid, 256, 0, stream>>>(K, width, prefix, rank, hist, out,
+                                                             p == passes - 1 ? 1 : 0);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// ---- alpha search -----------------------------------------------------------
+
+__device__ __forceinline__ double to_f64(uint16_t b) {
+    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(b) << 16));
+}
+__device__ __forceinline__ double to_f64(float v) { return static_cast<double>(v); }
+__device__ __forceinline__ float to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+// Y[m, n] = sum_k X[m, k] W[n, k] in fp64 (the inputs' products are exact in
+// fp64).  64 x 64 output tile per block, 4 x 4 outputs per thread (rows ty +
+// 16 i, columns tx + 16 j), K in steps of 16 staged in LDS.
+constexpr int kRT = 64;
+constexpr int kRK = 16;
+
+template <typename TX, typename TW>
+__global__ __launch_bounds__(256) void ref_gemm_f64_kernel(const TX* __restrict__ x,
+                                                           const TW* __restrict__ w, int64_t M,
+                                                           int64_t N, int64_t K,
+                                                           double* __restrict__ y) {
+    __shared__ double As[kRK][kRT + 1];
+    __shared__ double Bs[kRK][kRT + 1];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRT;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRT;
+    double acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int64_t k0 = 0; k0 < K; k0 += kRK) {
+        for (int i = threadIdx.x; i < kRT * kRK; i += 256) {
+            const int r = i / kRK, kk = i % kRK;
+            const int64_t k = k0 + kk;
+            const int64_t m = m0 + r, n = n0 + r;
+            As[kk][r] = (m < M && k < K) ? to_f64(x[m * K + k]) : 0.0;
+            Bs[kk][r] = (n < N && k < K) ? to_f64(w[n * K + k]) : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kRK; ++kk) {
+            double a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + ty + 16 * i, n = n0 + tx + 16 * j;
+            if (m < M && n < N) y[m * N + n] = acc[i][j];
+        }
+}
+
+constexpr int kEBlocks = 1024;   // partial sums per reduction
+constexpr int kEThreads = 256;
+
+// Block sum of two fp64 values in a fixed order (every lane's sequential sum,
+// then a fixed tree); thread 0 writes the block's pair.
+__device__ __forceinline__ void block_pair_sum(double a, double b, double* __restrict__ out) {
+    __shared__ double ra[kEThreads], rb[kEThreads];
+    ra[threadIdx.x] = a;
+    rb[threadIdx.x] = b;
+    __syncthreads();
+    for (int d = kEThreads / 2; d >= 1; d >>= 1) {
+        if (static_cast<int>(threadIdx.x) < d) {
+            ra[threadIdx.x] += ra[threadIdx.x + d];
+            rb[threadIdx.x] += rb[threadIdx.x + d];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = ra[0];
+        out[2 * blockIdx.x + 1] = rb[0];
+    }
+}
+
+// sum (y_q - y)^2 and sum y^2 over n outputs.
+__global__ __launch_bounds__(kEThreads) void out_err_kernel(const float* __restrict__ yq,
+                                                           const double* __restrict__ y,
+                                                           int64_t n, double* __restrict__ part) {
+    double a = 0.0, b = 0.0;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kEThreads + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * kEThreads) {
+        const double r = y[i];
+        const double d = static_cast<double>(yq[i]) - r;
+        a += d * d;
+        b += r * r;
+    }
+    block_pair_sum(a, b, part);
+}
+
+// sum (W^ - dw q)^2 and sum W^^2 with W^ = RN(W s) in fp32 (as the weight
+// quantizer forms it) and dw the row's step (or the tensor's).
+template <typename TW>
+__global__ __launch_bounds__(kEThreads) void w_err_kernel(
+    const TW* __restrict__ w, const float* __restrict__ s, const int8_t* __restrict__ wq,
+    const float* __restrict__ w_scale, int per_tensor, int64_t N, int64_t K,
+    double* __restrict__ part) {
+    double a = 0.0, b = 0.0;
+    const int64_t n_el = N * K;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kEThreads + threadIdx.x; i < n_el;
+         i += static_cast<int64_t>(gridDim.x) * kEThreads) {
+        const int64_t row = i / K, k = i - row * K;
+        const float what = to_f32(w[i]) * s[k];
+        const double dq = static_cast<double>(wq[i]) *
+                          static_cast<double>(w_scale[per_tensor ? 0 : row]);
+        const double d = static_cast<double>(what) - dq;
+        a += d * d;
+        b += static_cast<double>(what) * static_cast<double>(what);
+    }
+    block_pair_sum(a, b, part);
+}
+
+// One block: the partial pairs summed in a fixed order; out = num / den, or
+// num when den is 0.
+__global__ __launch_bounds__(kEThreads) void finish_ratio_kernel(const double* __restrict__ part,
+                                                                 int nparts,
+                                                                 double* __restrict__ out) {
+    __shared__ double ra[kEThreads], rb[kEThreads];
+    double a = 0.0, b = 0.0;
+    for (int i = threadIdx.x; i < nparts; i += kEThreads) {
+        a += part[2 * i];
+        b += part[2 * i + 1];
+    }
+    ra[threadIdx.x] = a;
+    rb[threadIdx.x] = b;
+    __syncthreads();
+    for (int d = kEThreads / 2; d >= 1; d >>= 1) {
+        if (static_cast<int>(threadIdx.x) < d) {
+            ra[threadIdx.x] += ra[threadIdx.x + d];
+            rb[threadIdx.x] += rb[threadIdx.x + d];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = rb[0] > 0.0 ? ra[0] / rb[0] : ra[0];
+}
+
+// The first index of the least value.
+__global__ void argmin_kernel(const double* __restrict__ v, int n, int32_t* __restrict__ best) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int b = 0;
+    for (int i = 1; i < n; ++i)
+        if (v[i] < v[b]) b = i;
+    *best = b;
+}
+
+template <typename TX, typename TW>
+hipError_t run_ref_gemm(const void* x, const void* w, int64_t M, int64_t N, int64_t K, double* y,
+                        hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((N + kRT - 1) / kRT),
+                    static_cast<unsigned>((M + kRT - 1) / kRT));
+    ref_gemm_f64_kernel<TX, TW><<<grid, 256, 0, stream>>>(static_cast<const TX*>(x),
+                                                          static_cast<const TW*>(w), M, N, K, y);
+    return hipGetLastError();
+}
+
+// Workspace carving: 256-byte aligned sections.
+struct AlphaWs {
+    double* yref;
+    float* yq;
+    int8_t* xq;
+    float* xs;
+    float* s;
+    int8_t* wq;
+    float* ws;
+    float* st;
+    float* xa;
+    float* wa;
+    double* part;
+    size_t bytes;
+};
+
+AlphaWs carve(void* base, int64_t T, int64_t N, int64_t K) {
+    uintptr_t p = reinterpret_cast<uintptr_t>(base);
+    const uintptr_t p0 = p;
+    auto take = [&](size_t n) {
+        const uintptr_t r = p;
+        p += (n + 255) & ~static_cast<size_t>(255);
+        return r;
+    };
+    AlphaWs a;
+    a.yref = reinterpret_cast<double*>(take(static_cast<size_t>(T * N) * 8));
+    a.yq = reinterpret_cast<float*>(take(static_cast<size_t>(T * N) * 4));
+    a.xq = reinterpret_cast<int8_t*>(take(static_cast<size_t>(T * K)));
+    a.xs = reinterpret_cast<float*>(take(static_cast<size_t>(std::max<int64_t>(T, 1)) * 4));
+    a.s = reinterpret_cast<float*>(take(static_cast<size_t>(K) * 4));
+    a.wq = reinterpret_cast<int8_t*>(take(static_cast<size_t>(N * K)));
+    a.ws = reinterpret_cast<float*>(take(static_cast<size_t>(std::max<int64_t>(N, 1)) * 4));
+    a.st = reinterpret_cast<float*>(take(16));
+    a.xa = reinterpret_cast<float*>(take(static_cast<size_t>(K) * 4));
+    a.wa = reinterpret_cast<float*>(take(static_cast<size_t>(K) * 4));
+    a.part = reinterpret_cast<double*>(take(static_cast<size_t>(kEBlocks) * 16));
+    a.bytes = p - p0;
+    return a;
+}
+
+}  // namespace
+
+size_t quantile_workspace_bytes(int64_t K) {
+    return static_cast<size_t>(K) * (kQBins * 4 + 8) + 256;
+}
+
+hipError_t launch_channel_quantile(const void* x, Dt x_dt, int64_t T, int64_t K, int64_t rank,
+                                   float* out, void* ws, hipStream_t stream) {
+    uint32_t* hist = static_cast<uint32_t*>(ws);
+    uint32_t* prefix = hist + K * kQBins;
+    uint32_t* rk = prefix + K;
+    return (x_dt == Dt::BF16)
+               ? run_quantile(static_cast<const uint16_t*>(x), T, K, rank, out, hist, prefix, rk,
+                              stream)
+               : run_quantile(static_cast<const float*>(x), T, K, rank, out, hist, prefix, rk,
+                              stream);
+}
+
+size_t alpha_workspace_bytes(int64_t T, int64_t N, int64_t K) {
+    return carve(nullptr, T, N, K).bytes;
+}
+
+hipError_t launch_alpha_search(const void* x_cal, Dt x_dt, int64_t T, const void* w, Dt w_dt,
+                               int64_t N, int64_t K, const float* alphas, int n_alpha,
+                               ActMode mode, bool w_per_tensor, double* err, double* werr,
+                               int32_t* best, void* ws, hipStream_t stream) {
+    const AlphaWs a = carve(ws, T, N, K);
+    hipError_t e;
+    if (x_dt == Dt::BF16)
+        e = (w_dt == Dt::BF16) ? run_ref_gemm<uint16_t, uint16_t>(x_cal, w, T, N, K, a.yref, stream)
+                               : run_ref_gemm<uint16_t, float>(x_cal, w, T, N, K, a.yref, stream);
+    else
+        e = (w_dt == Dt::BF16) ? run_ref_gemm<float, uint16_t>(x_cal, w, T, N, K, a.yref, stream)
+                               : run_ref_gemm<float, float>(x_cal, w, T, N, K, a.yref, stream);
+    if (e != hipSuccess) return e;
+    const bool st = mode == ActMode::Static;
+    for (int i = 0; i < n_alpha; ++i) {
+        e = launch_calibrate(x_cal, x_dt, T, w, w_dt, N, K, alphas[i], w_per_tensor, nullptr,
+                             nullptr, a.s, a.wq, a.ws, a.st, nullptr, nullptr, a.xa, a.wa,
+                             nullptr, stream);
+        if (e != hipSuccess) return e;
+        e = launch_act_quant(x_cal, x_dt, T, K, a.s, nullptr, nullptr, 1e-5f, mode,
+                             st ? a.st : nullptr, a.xq, a.xs, stream);
+        if (e != hipSuccess) return e;
+        e = launch_gemm(a.xq, st ? a.st : a.xs, mode == ActMode::PerToken, a.wq, a.ws,
+                        w_per_tensor, T, N, K, a.yq, 0, Epi{}, Batch{}, stream);
+        if (e != hipSuccess) return e;
+        out_err_kernel<<<kEBlocks, kEThreads, 0, stream>>>(a.yq, a.yref, T * N, a.part);
+        finish_ratio_kernel<<<1, kEThreads, 0, stream>>>(a.part, kEBlocks, err + i);
+        if (w_dt == Dt::BF16)
+            w_err_kernel<uint16_t><<<kEBlocks, kEThreads, 0, stream>>>(
+                static_cast<const uint16_t*>(w), a.s, a.wq, a.ws, w_per_tensor ? 1 : 0, N, K,
+                a.part);
+        else
+            w_err_kernel<float><<<kEBlocks, kEThreads, 0, stream>>>(
+                static_cast<const float*>(w), a.s, a.wq, a.ws, w_per_tensor ? 1 : 0, N, K, a.part);
+        finish_ratio_kernel<<<1, kEThreads, 0, stream>>>(a.part, kEBlocks, werr + i);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    argmin_kernel<<<1, 64, 0, stream>>>(err, n_alpha, best);
+    return hipGetLastError();
+}
+
+}  // namespace sq

@@ -20,7 +20,21 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
                             int64_t N, int64_t K, float alpha, bool w_per_tensor, const float* gamma,
                             const float* beta, float* s, int8_t* wq, float* w_scale,
                             float* act_scale_static, float* gamma_s, float* beta_s,
-                            float* x_absmax, float* w_absmax, hipStream_t stream);
+                            float* x_absmax, float* w_absmax, const float* act_stat,
+                            hipStream_t stream);
+
+// Saturation count of the static quantizer (count mode: no codes written);
+// *clip and clip_ch[K] (optional) are overwritten.
+hipError_t launch_clip_count(const void* x, Dt x_dt, int64_t M, int64_t K, const float* s,
+                             const float* gamma_s, const float* beta_s, float eps,
+                             const float* static_scale, unsigned long long* clip,
+                             uint32_t* clip_ch, hipStream_t stream);
+
+// Robust calibration: the nearest-rank quantile (rank 1..T) of |x[:, j]| per
+// channel into out[K] (floored); workspace of quantile_workspace_bytes(K).
+size_t quantile_workspace_bytes(int64_t K);
+hipError_t launch_channel_quantile(const void* x, Dt x_dt, int64_t T, int64_t K, int64_t rank,
+                                   float* out, void* ws, hipStream_t stream);
 
 // Activation smoothing + quantization (runtime).
 hipError_t launch_act_quant(const void* x, Dt x_dt, int64_t M, int64_t K, const float* s,
@@ -57,5 +71,14 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
                        const int8_t* wq, const float* w_scale, bool w_per_tensor, int64_t M,
                        int64_t N, int64_t K, void* y, int out_kind, const Epi& epi,
                        const Batch& bat, hipStream_t stream);
+
+// Alpha search over candidate smoothing strengths (host array alphas[n]):
+// err[i], werr[i] (device fp64) and best (device); workspace of
+// alpha_workspace_bytes(T, N, K).
+size_t alpha_workspace_bytes(int64_t T, int64_t N, int64_t K);
+hipError_t launch_alpha_search(const void* x_cal, Dt x_dt, int64_t T, const void* w, Dt w_dt,
+                               int64_t N, int64_t K, const float* alphas, int n_alpha,
+                               ActMode mode, bool w_per_tensor, double* err, double* werr,
+                               int32_t* best, void* ws, hipStream_t stream);
 
 }  // namespace sq
