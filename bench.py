@@ -36,7 +36,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SRC = os.path.join(ROOT, "w8a8_int8_gemm_colwise_amd", "csrc", "gemm.hip")
 
 WORKLOADS = {"opt6.7b": 2, "decode70b": 3, "opt175b": 4, "ln8192": 5, "single512": 1,
-             "attn6.7b": None}
+             "attn6.7b": None, "robust8192": None}
 # OPT-6.7B self-attention at 2048 tokens: 32 heads of dimension 128
 ATTN_HEADS, ATTN_SEQ, ATTN_HD = 32, 2048, 128
 
@@ -264,6 +264,126 @@ def bench_attention(args, attain_fn):
     return out
 
 
+def bench_robust(args, attain_fn):
+    """Robust calibration on the LayerNorm workload (hidden 8192): the 0.999
+    channel quantile of the 65536-token bf16 calibration set (1 GiB; the peak
+    pass of sq_calibrate on the same set beside it), the clip count of the
+    4096 evaluation tokens under the quantile's static step, and the alpha
+    search (6 candidates) of the OPT-6.7B qkv linear on its 512 calibration
+    tokens."""
+    import torch
+
+    import datagen
+    import w8a8_int8_gemm_colwise_amd as sq
+
+    dev = torch.device("cuda:0")
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    spec = datagen.workload(5).layers[0]
+    xc = bf(datagen.calibration_x(spec))
+    w = bf(datagen.weights(spec))
+    x = bf(datagen.eval_x(spec))
+    g, b = (torch.from_numpy(t).to(dev) for t in datagen.ln_params(spec))
+    q_spec = datagen.workload(2).layers[0]
+    xq_cal, wq_lin = bf(datagen.calibration_x(q_spec)), bf(datagen.weights(q_spec))
+    T, K = xc.shape
+    N = w.shape[0]
+    M = x.shape[0]
+    alphas = [0.0, 0.25, 0.5, 0.75, 0.85, 1.0]
+    ws_q = torch.empty(sq.lib().sq_channel_quantile_workspace_size(K), dtype=torch.uint8,
+                       device=dev)
+    stat = torch.empty(K, dtype=torch.float32, device=dev)
+    Tq, Kq = xq_cal.shape
+    Nq = wq_lin.shape[0]
+    ws_a = torch.empty(sq.lib().sq_alpha_search_workspace_size(Tq, Nq, Kq), dtype=torch.uint8,
+                       device=dev)
+    cal_out = None
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        nonlocal cal_out
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        sq.sq_channel_quantile(xc, 0.999, out=stat, workspace=ws_q)
+        mark(1)
+        cal_out = sq.sq_calibrate(xc, w, 0.5, g, b, out=cal_out)
+        mark(2)
+        rob = sq.sq_calibrate_stat(stat, w, 0.5, g, b)
+        mark(3)
+        sq.sq_clip_count(x, rob["static_scale"], ln_gamma_s=rob["ln_gamma_s"],
+                         ln_beta_s=rob["ln_beta_s"], per_channel=True)
+        mark(4)
+        sq.sq_alpha_search(xq_cal, wq_lin, alphas, workspace=ws_a)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t = np.zeros(5)
+    for e in evs:
+        for i in range(5):
+            t[i] += e[i].elapsed_time(e[i + 1]) * 1e-3
+    t /= args.steps
+    x_bytes = T * K * 2
+    b_quant = x_bytes + 4 * K                                 # one read of X_cal
+    b_peak = x_bytes + N * K * 2 * 2 + N * K + 4 * N          # sq_calibrate: X, W twice, Wq
+    b_stat = N * K * 2 * 2 + N * K + 4 * N                    # from a statistic: W twice, Wq
+    b_clip = M * K * 2 + 4 * K
+    ref_flops = 2.0 * Tq * Nq * Kq
+    per = {
+        "channel_quantile_q0.999": {"us": round(t[0] * 1e6, 1),
+                                    "GBs_alg": round(b_quant / t[0] / 1e9, 1),
+                                    "passes_over_x": 2,
+                                    "GBs_read": round(2 * x_bytes / t[0] / 1e9, 1)},
+        "calibrate_peak": {"us": round(t[1] * 1e6, 1), "GBs_alg": round(b_peak / t[1] / 1e9, 1)},
+        "calibrate_stat": {"us": round(t[2] * 1e6, 1), "GBs_alg": round(b_stat / t[2] / 1e9, 1)},
+        "clip_count_ln": {"us": round(t[3] * 1e6, 1), "GBs_alg": round(b_clip / t[3] / 1e9, 1)},
+        "alpha_search_6": {"us": round(t[4] * 1e6, 1),
+                           "us_per_alpha": round(t[4] / len(alphas) * 1e6, 1),
+                           "shape_TNK": [Tq, Nq, Kq]},
+    }
+    ach = b_quant / t[0] / 1e9
+    roof = {"kernel": "sq_channel_quantile (quantile_hist_kernel + select)", "bound": "hbm",
+            "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "launches_per_step": 1,
+            "avg_launch_us": round(t[0] * 1e6, 2), "alg_bytes_per_launch": b_quant}
+    attain = attain_fn(dev)
+    if attain:
+        roof["attainable"] = attain["hbm_read_GBs"]
+        roof["frac_attainable"] = round(ach / attain["hbm_read_GBs"], 4)
+    out = {
+        "metric": "W8A8 GEMM INT8 TOPS (% MFMA peak) + fused quantize GB/s (% HBM peak)",
+        "value": round(b_quant / t[0] / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded LayerNorm-workload tokens with 0.5% outlier channels)",
+        "config": {"workload": "robust calibration, hidden 8192: quantile of 65536 x 8192 "
+                               "calibration tokens; clip count of 4096 tokens; alpha search "
+                               "of a 512 x 4096 -> 12288 linear",
+                   "q": 0.999, "alphas": alphas,
+                   "step": "sq_channel_quantile; sq_calibrate; sq_calibrate_stat; "
+                           "sq_clip_count; sq_alpha_search"},
+        "roofline": roof,
+        "per_call": per,
+    }
+    if attain:
+        out["attainable"] = attain
+    return out
+
+
 def _attainable(args):
     def fn(dev):
         if args.no_probes:
@@ -307,6 +427,9 @@ def main():
         sys.exit(2)
     if args.workload == "attn6.7b":
         print(json.dumps(bench_attention(args, _attainable(args))), flush=True)
+        return
+    if args.workload == "robust8192":
+        print(json.dumps(bench_robust(args, _attainable(args))), flush=True)
         return
 
     import torch
