@@ -422,7 +422,7 @@ def main():
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU sharding).", file=sys.stderr)
         sys.exit(2)
     if args.workload == "attn6.7b":
