@@ -502,17 +502,35 @@ struct Split {
     int64_t rpb = 0;
 };
 
-// Column segments x row splits for one tensor: about one block of 16 waves
-// per CU in total, at least 128 rows per block.
-Split plan_split(int64_t rows, int64_t K, int seg_cols) {
-    Split p;
-    if (rows <= 0) return p;
-    p.segs = static_cast<int>((K + seg_cols - 1) / seg_cols);
-    const int64_t want = (256 + p.segs - 1) / p.segs;
-    const int64_t by = std::max<int64_t>(1, std::min<int64_t>(want, (rows + 127) / 128));
-    p.rpb = (rows + by - 1) / by;
-    p.splits = static_cast<int>((rows + p.rpb - 1) / p.rpb);
-    return p;
+// X_cal and W in one launch of equal blocks: every block covers one column
+// segment (1 KB of a row for either dtype) over the same number of rows r, the
+// least r >= 128 for which all blocks fit in one round of 256 (one 16-wave
+// block per CU); separate splits of X_cal and W would leave a second round of
+// blocks on some CUs.
+void plan_joint(int64_t T, int64_t N, int64_t K, int seg_x, int seg_w, Split& px, Split& pw) {
+    px = Split{};
+    pw = Split{};
+    const int sx = T > 0 ? static_cast<int>((K + seg_x - 1) / seg_x) : 0;
+    const int sw = N > 0 ? static_cast<int>((K + seg_w - 1) / seg_w) : 0;
+    if (sx + sw == 0) return;
+    const int64_t rowsegs = T * sx + N * sw;
+    int64_t r = std::max<int64_t>(128, (rowsegs + 255) / 256);
+    const int64_t rmax = std::max<int64_t>(T, N);
+    for (;;) {
+        const int64_t blocks = sx * ((T + r - 1) / r) + sw * ((N + r - 1) / r);
+        if (blocks <= 256 || r >= rmax) break;
+        r += std::max<int64_t>(1, r / 32);
+    }
+    if (T > 0) {
+        px.segs = sx;
+        px.splits = static_cast<int>((T + r - 1) / r);
+        px.rpb = (T + px.splits - 1) / px.splits;
+    }
+    if (N > 0) {
+        pw.segs = sw;
+        pw.splits = static_cast<int>((N + r - 1) / r);
+        pw.rpb = (N + pw.splits - 1) / pw.splits;
+    }
 }
 
 template <typename TX, typename TW>
@@ -548,8 +566,8 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
     // The per-block column maxima need (splits_x + splits_w) * K words of
     // scratch; the int8 weight output, written only by the last kernel, holds
     // them when it is large enough.  Otherwise: fill + atomic column maxima.
-    const Split px = plan_split(T, K, x_dt == Dt::BF16 ? 512 : 256);
-    const Split pw = plan_split(N, K, w_dt == Dt::BF16 ? 512 : 256);
+    Split px, pw;
+    plan_joint(T, N, K, x_dt == Dt::BF16 ? 512 : 256, w_dt == Dt::BF16 ? 512 : 256, px, pw);
     const int64_t need = static_cast<int64_t>(px.splits + pw.splits) * K * 4;
     const bool use_partial = N > 0 && need <= N * K;
     uint32_t* partial = use_partial ? reinterpret_cast<uint32_t*>(wq) : nullptr;
