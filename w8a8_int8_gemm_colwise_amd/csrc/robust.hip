@@ -96,30 +96,61 @@ __global__ __launch_bounds__(kQThreads) void quantile_hist_kernel(
     }
 }
 
-// One thread per column: the bin of the digit that holds the remaining rank
-// extends the prefix; the histogram row is cleared for the next pass.  After
-// the last pass the prefix is the whole magnitude pattern of the quantile.
+// One wave per column: lane l holds bins 4l..4l+3 of the column's histogram
+// (one 16-byte read each); an inclusive scan over the lanes finds the lane,
+// then the bin, where the cumulative count first reaches the remaining rank.
+// That bin extends the prefix, the rank drops by the count before it, and the
+// histogram row is cleared for the next pass.  After the last pass the prefix
+// is the whole magnitude pattern of the quantile.
 template <typename T>
 __global__ __launch_bounds__(256) void quantile_select_kernel(
     int64_t K, int width, uint32_t* __restrict__ prefix, uint32_t* __restrict__ rank,
     uint32_t* __restrict__ hist, float* __restrict__ out, int last) {
-    const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (col >= K) return;
-    uint32_t* hc = hist + col * kQBins;
-    const uint32_t r = rank[col];
-    const int nb = 1 << width;
-    uint32_t cum = 0u;
-    int b = 0;
-    for (; b < nb - 1; ++b) {
-        const uint32_t c = hc[b];
-        if (cum + c >= r) break;
-        cum += c;
+    const int lane = threadIdx.x & 63;
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (col >= K) return;  // whole waves
+    uint4* hc = reinterpret_cast<uint4*>(hist + col * kQBins);
+    const uint4 h = hc[lane];
+    const uint32_t lsum = h.x + h.y + h.z + h.w;
+    uint32_t incl = lsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = static_cast<uint32_t>(__shfl_up(static_cast<int>(incl), o, 64));
+        if (lane >= o) incl += t;
     }
-    for (int i = 0; i < nb; ++i) hc[i] = 0u;
-    const uint32_t p = (prefix[col] << width) | static_cast<uint32_t>(b);
-    prefix[col] = p;
-    rank[col] = r - cum;
-    if (last) out[col] = fmaxf(Mag<T>::value(p), kFloor);
+    const uint32_t r = rank[col];
+    uint32_t cum = incl - lsum;
+    const bool mine = cum < r && r <= incl;
+    int b = 3;
+    if (mine) {
+        const uint32_t c[4] = {h.x, h.y, h.z, h.w};
+        for (b = 0; b < 3; ++b) {
+            if (cum + c[b] >= r) break;
+            cum += c[b];
+        }
+    }
+    const unsigned long long bal = __ballot(mine);
+    hc[lane] = make_uint4(0u, 0u, 0u, 0u);
+    int bin;
+    uint32_t before;
+    if (bal) {
+        const int src = __ffsll(static_cast<long long>(bal)) - 1;
+        bin = __shfl(4 * lane + b, src, 64);
+        before = static_cast<uint32_t>(__shfl(static_cast<int>(cum), src, 64));
+    } else {
+        // counts short of the rank (not reached with consistent counts): the
+        // last bin, where a sequential scan of the histogram would stop
+        const int nb = 1 << width;  // 128 or 256: bin nb - 1 is component w of lane nb/4 - 1
+        bin = nb - 1;
+        const uint32_t last = static_cast<uint32_t>(__shfl(static_cast<int>(h.w), nb / 4 - 1, 64));
+        before = static_cast<uint32_t>(__shfl(static_cast<int>(incl), 63, 64)) - last;
+    }
+    if (lane == 0) {
+        const uint32_t p = (prefix[col] << width) | static_cast<uint32_t>(bin);
+        prefix[col] = p;
+        rank[col] = r - before;
+        if (last) out[col] = fmaxf(Mag<T>::value(p), kFloor);
+    }
 }
 
 __global__ __launch_bounds__(256) void quantile_init_kernel(int64_t K, uint32_t rank0,
@@ -153,7 +184,7 @@ hipError_t run_quantile(const T* x, int64_t rows, int64_t K, int64_t rank0, floa
     const int64_t splits = std::min<int64_t>({want, (rows + 255) / 256, 65535});
     const int64_t rpb = (rows + splits - 1) / splits;
     const dim3 hgrid(static_cast<unsigned>(strips), static_cast<unsigned>((rows + rpb - 1) / rpb));
-    const unsigned sgrid = static_cast<unsigned>((K + 255) / 256);
+    const unsigned sgrid = static_cast<unsigned>((K + 3) / 4);
     constexpr int NB = Mag<T>::kBits;
     const int passes = (NB + 7) / 8;
     for (int p = 0; p < passes; ++p) {
@@ -177,10 +208,6 @@ __device__ __forceinline__ double to_f64(uint16_t b) {
     return static_cast<double>(__uint_as_float(static_cast<uint32_t>(b) << 16));
 }
 __device__ __forceinline__ double to_f64(float v) { return static_cast<double>(v); }
-__device__ __forceinline__ float to_f32(uint16_t b) {
-    return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-__device__ __forceinline__ float to_f32(float v) { return v; }
 
 // Y[m, n] = sum_k X[m, k] W[n, k] in fp64 (the inputs' products are exact in
 // fp64).  64 x 64 output tile per block, 4 x 4 outputs per thread (rows ty +
@@ -274,23 +301,34 @@ __global__ __launch_bounds__(kEThreads) void out_err_kernel(const float* __restr
 }
 
 // sum (W^ - dw q)^2 and sum W^^2 with W^ = RN(W s) in fp32 (as the weight
-// quantizer forms it) and dw the row's step (or the tensor's).
+// quantizer forms it) and dw the row's step (or the tensor's); blocks walk
+// rows, threads 8-element chunks of a row (K % 64 == 0).
 template <typename TW>
 __global__ __launch_bounds__(kEThreads) void w_err_kernel(
     const TW* __restrict__ w, const float* __restrict__ s, const int8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int per_tensor, int64_t N, int64_t K,
     double* __restrict__ part) {
     double a = 0.0, b = 0.0;
-    const int64_t n_el = N * K;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kEThreads + threadIdx.x; i < n_el;
-         i += static_cast<int64_t>(gridDim.x) * kEThreads) {
-        const int64_t row = i / K, k = i - row * K;
-        const float what = to_f32(w[i]) * s[k];
-        const double dq = static_cast<double>(wq[i]) *
-                          static_cast<double>(w_scale[per_tensor ? 0 : row]);
-        const double d = static_cast<double>(what) - dq;
-        a += d * d;
-        b += static_cast<double>(what) * static_cast<double>(what);
+    const int64_t chunks = K / kChunk;
+    for (int64_t row = blockIdx.x; row < N; row += gridDim.x) {
+        const double dw = static_cast<double>(w_scale[per_tensor ? 0 : row]);
+        const TW* wr = w + row * K;
+        const int8_t* qr = wq + row * K;
+        for (int64_t c = threadIdx.x; c < chunks; c += kEThreads) {
+            float v[kChunk], sv[kChunk];
+            load_chunk(wr, c, v);
+            load_chunk(s, c, sv);
+            const uint2 q8 = *reinterpret_cast<const uint2*>(qr + c * kChunk);
+            const uint32_t qw[2] = {q8.x, q8.y};
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                const float what = v[e] * sv[e];
+                const int q = static_cast<int8_t>((qw[e >> 2] >> (8 * (e & 3))) & 0xffu);
+                const double d = static_cast<double>(what) - static_cast<double>(q) * dw;
+                a += d * d;
+                b += static_cast<double>(what) * static_cast<double>(what);
+            }
+        }
     }
     block_pair_sum(a, b, part);
 }
