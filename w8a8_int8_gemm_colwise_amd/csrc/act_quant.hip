@@ -9,14 +9,19 @@
 //   §二: the LayerNorm with gamma/s and beta/s folded in emits the smoothed
 //   activation directly, followed by int8 quantization.
 //
-// One token row per block.  The block's lanes own fixed chunks of 8 elements
-// (chunk c = tid + i*blockDim), so per-column data (1/s_k) is computed once
-// per block and reused across the rows the block walks.  The row stays in
-// registers between the absmax reduction and the quantize pass.  Divisions
-// by s_k and by the step use div_rn() (correctly rounded, five VALU ops).
-// LayerNorm mode uses exactly 256 lanes so that lane t owns partial t of the
-// canonical fp32 reduction (chunk c -> partial c mod 256, increasing k within
-// a partial, then the fixed halving tree).
+// act_quant_kernel: one token row per block.  The block's lanes own fixed
+// chunks of 8 elements (chunk c = tid + i*blockDim), so per-column data
+// (1/s_k) is computed once per block and reused across the rows the block
+// walks.  The row stays in registers between the absmax reduction and the
+// quantize pass.  Divisions by s_k and by the step use div_rn() (correctly
+// rounded, five VALU ops).  LayerNorm mode uses exactly 256 lanes so that lane
+// t owns partial t of the canonical fp32 reduction (chunk c -> partial c mod
+// 256, increasing k within a partial, then the fixed halving tree).
+// act_quant_rows_kernel packs several short rows (K <= 256) into a wave;
+// act_quant_stream_kernel re-reads long rows per sweep.  All three share the
+// per-element arithmetic and have a row-maximum pass (the first pass of the
+// dynamic per-tensor step) and a count mode (the static quantizer's
+// saturation count, no codes written).
 #include <algorithm>
 
 #include "sq_device.hpp"

@@ -8,16 +8,29 @@
 //   §2.6 / Fig. 3: scales live on the outer dimensions (token, output
 //   channel) so they factor out of the contraction.
 //
+//   [Review] §5.6 / Fig. 6: the batched products of attention run in int8 as
+//   well (every kernel takes a batch index on grid.y, see Batch).
+//
 // Y[M, N] = Xq[M, K] . Wq[N, K]^T: both operands are K-contiguous ("NT"), the
 // layout the MFMA operand registers want (16 consecutive int8 of one row per
-// lane).  Each block owns a BM x BN tile of Y; K advances in 64-byte tiles
-// staged through LDS with two buffers (global loads for tile k+1 are in flight
-// while the matrix cores work on tile k).  Each wave owns a WM x WN sub-tile
-// made of 32x32 v_mfma_i32_32x32x32_i8 tiles accumulated in int32 registers.
-// LDS rows are 64 bytes; the 16-byte chunk c of row r is stored at chunk
-// c ^ swz(r) so that the operand fetches (ds_read_b128) hit distinct banks.
-// Blocks are remapped so that the tiles one XCD runs are neighbours (sharing
-// A rows and B columns in that XCD's L2).
+// lane); 32x32 v_mfma_i32_32x32x32_i8 tiles accumulate in int32 registers.
+// Kernels, chosen by launch_gemm from the shape:
+//   gemm_pp_kernel      M > 64, K % 128 == 0: 256x128 or 256x256 tiles, eight
+//                       waves in two groups alternating memory and compute
+//                       phases ("ping-pong"), three LDS stages filled by
+//                       direct-to-LDS transfers
+//   gemm_shortk_kernel  M > 64, K in {64, 128, 256}: the tile's whole K in LDS
+//                       at once, several blocks per CU (store-bound shapes such
+//                       as the attention scores)
+//   gemm_skinny_kernel  M <= 64 (decode): a weight stream, K split over the
+//                       waves of a block with per-wave LDS rings
+//   gemm_kernel         the rest: register-staged, two LDS buffers
+// The pipelined kernels dequantize through a transposed epilogue (store_tile_t)
+// that leaves each tile as whole 16-byte chunks of 128-byte row segments; the
+// optional fused epilogue (Epi) adds bias, ReLU, or writes the next linear's
+// int8 codes.  LDS chunks are XOR-swizzled so operand fetches hit distinct
+// banks, and blocks are remapped so that the tiles one XCD runs are neighbours
+// (sharing A rows and B columns in that XCD's L2).
 #include <type_traits>
 
 #include "sq_device.hpp"
