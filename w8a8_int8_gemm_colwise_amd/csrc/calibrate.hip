@@ -210,74 +210,90 @@ hipError_t launch_colmax(const T* x, int64_t rows, int64_t K, uint32_t* out_bits
 
 // ---- smoothing factor, fold, static scale ------------------------------------
 
-constexpr int kFactorThreads = 64;  // many small blocks: the pass is latency-bound
+constexpr int kFactorCols = 64;   // columns per block, one per lane
+constexpr int kFactorWaves = 4;   // waves that split a column's per-block maxima
+constexpr int kFactorThreads = 64 * kFactorWaves;
 
 // With `partial` set, first reduce the per-block column maxima of X_cal (rows
 // [0, splits_x)) and W (rows [splits_x, splits_x + splits_w)) into a_j and w_j
-// (floored) and store them; otherwise a_j and w_j are already in a and w.
+// (floored) and store them; otherwise a_j and w_j are already in a and w.  The
+// pass is latency-bound: wave g of a block takes partial rows g, g + 4, ...
+// of the block's 64 columns (eight loads in flight per batch), the four
+// results meet in LDS, and wave 0 finishes the columns (eq. (4), fold, static
+// scale).
 __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
     float* __restrict__ a, float* __restrict__ w, int64_t K, float alpha,
     const uint32_t* __restrict__ partial, int splits_x, int splits_w,
     const float* __restrict__ gamma, const float* __restrict__ beta, float* __restrict__ s,
     float* __restrict__ gamma_s, float* __restrict__ beta_s, uint32_t* __restrict__ static_bits,
     const float* __restrict__ act_stat) {
-    __shared__ float red[kFactorThreads / 64];
+    __shared__ uint32_t pm[2][kFactorWaves][kFactorCols];
+    const int lane = threadIdx.x & 63;
+    const int g = threadIdx.x >> 6;
     const double al = static_cast<double>(alpha);
     const double be = 1.0 - al;
     float local = 0.0f;
-    for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < K;
-         j += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        float aj, wj;
+    for (int64_t j0 = static_cast<int64_t>(blockIdx.x) * kFactorCols; j0 < K;
+         j0 += static_cast<int64_t>(gridDim.x) * kFactorCols) {
+        const int64_t j = j0 + lane;
         if (partial) {
-            // eight independent loads in flight per batch
             auto reduce = [&](int first, int count) {
                 uint32_t m = kFloorBits;
-                for (int i = 0; i < count; i += 8) {
+                for (int i = g; i < count; i += 8 * kFactorWaves) {
                     uint32_t v[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        v[u] = (i + u < count) ? partial[(first + i + u) * K + j] : 0u;
+                    for (int u = 0; u < 8; ++u) {
+                        const int r = i + u * kFactorWaves;
+                        v[u] = (r < count) ? partial[static_cast<int64_t>(first + r) * K + j] : 0u;
+                    }
 #pragma unroll
                     for (int u = 0; u < 8; ++u) m = max(m, v[u]);
                 }
                 return m;
             };
-            const uint32_t ab = reduce(0, splits_x);
-            const uint32_t wb = reduce(splits_x, splits_w);
-            aj = __uint_as_float(ab);
-            wj = __uint_as_float(wb);
-            a[j] = aj;
-            w[j] = wj;
-        } else {
-            aj = a[j];
-            wj = w[j];
+            pm[0][g][lane] = j < K ? reduce(0, splits_x) : kFloorBits;
+            pm[1][g][lane] = j < K ? reduce(splits_x, splits_w) : kFloorBits;
         }
-        if (act_stat) {
-            // a given per-channel activation statistic replaces the peak
-            aj = fmaxf(act_stat[j], kFloor);
-            a[j] = aj;
+        __syncthreads();
+        if (g == 0 && j < K) {
+            float aj, wj;
+            if (partial) {
+                uint32_t ab = pm[0][0][lane], wb = pm[1][0][lane];
+#pragma unroll
+                for (int q = 1; q < kFactorWaves; ++q) {
+                    ab = max(ab, pm[0][q][lane]);
+                    wb = max(wb, pm[1][q][lane]);
+                }
+                aj = __uint_as_float(ab);
+                wj = __uint_as_float(wb);
+                a[j] = aj;
+                w[j] = wj;
+            } else {
+                aj = a[j];
+                wj = w[j];
+            }
+            if (act_stat) {
+                // a given per-channel activation statistic replaces the peak
+                aj = fmaxf(act_stat[j], kFloor);
+                a[j] = aj;
+            }
+            // eq. (4) in fp64, rounded once to fp32
+            const float sj = static_cast<float>(pow(static_cast<double>(aj), al) /
+                                                pow(static_cast<double>(wj), be));
+            s[j] = sj;
+            if (gamma) {
+                gamma_s[j] = gamma[j] / sj;
+                beta_s[j] = beta[j] / sj;
+            }
+            // RN(max(FLOOR, x)/127) is monotone in x, so the max of the per-channel
+            // steps is the step of the max smoothed calibration peak RN(a_j/s_j).
+            local = fmaxf(local, step_from_absmax(aj / sj));
         }
-        // eq. (4) in fp64, rounded once to fp32
-        const float sj = static_cast<float>(pow(static_cast<double>(aj), al) /
-                                            pow(static_cast<double>(wj), be));
-        s[j] = sj;
-        if (gamma) {
-            gamma_s[j] = gamma[j] / sj;
-            beta_s[j] = beta[j] / sj;
-        }
-        // RN(max(FLOOR, x)/127) is monotone in x, so the max of the per-channel
-        // steps is the step of the max smoothed calibration peak RN(a_j/s_j).
-        local = fmaxf(local, step_from_absmax(aj / sj));
+        __syncthreads();  // pm is refilled by the next columns
     }
-    if (!static_bits) return;
+    if (!static_bits || g != 0) return;
     local = wave_max(local);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = local;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float m = red[0];
-        for (int i = 1; i < kFactorThreads / 64; ++i) m = fmaxf(m, red[i]);
-        atomicMax(static_bits, __float_as_uint(m));
-    }
+    if (lane == 0) atomicMax(static_bits, __float_as_uint(local));
 }
 
 // ---- weight smoothing + per-output-channel quantization ------------------------
@@ -594,7 +610,7 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
         if (e != hipSuccess) return e;
     }
 
-    const int64_t fgrid = std::min<int64_t>((K + kFactorThreads - 1) / kFactorThreads, 1024);
+    const int64_t fgrid = std::min<int64_t>((K + kFactorCols - 1) / kFactorCols, 1024);
     smooth_factor_kernel<<<static_cast<unsigned>(fgrid), kFactorThreads, 0, stream>>>(
         x_absmax, w_absmax, K, alpha, partial, px.splits, pw.splits, gamma, beta, s, gamma_s,
         beta_s, sb, act_stat);
