@@ -7,10 +7,13 @@ alpha = 0.5): for every linear, sq_calibrate (column absmax of the 512-token
 calibration set and of W, eq. (4), smoothed per-output-channel int8 weights),
 sq_smooth_quantize_act (X/s + per-token int8), sq_gemm_w8a8 (int8 GEMM with
 bf16 dequantized output).  Inputs are resident in HBM before timing starts.
+The timed steps replay the step captured once as a HIP graph (``--eager``:
+plain launches); a pass of eager steps with HIP events around every call on
+the launch stream gives the per-call times.
 
 Prints ONE JSON line.  ``value`` = int8 TOPS of the whole step (2*M*N*K summed
 over the four linears / step time).  ``roofline`` describes the dominant
-kernel (the GEMM) measured with HIP events on the launch stream; the
+kernel (the GEMM) from the per-call event times; the
 ``cpu_baseline`` leg times the CPU oracle on a bounded sample of the same
 workload on this host.
 
@@ -417,6 +420,8 @@ def main():
                          "activation quantizer call; fc2's GEMM reads a static per-tensor step")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the attainable-ceiling probes (MFMA loop, HBM read and copy)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches of the step instead of HIP graph replays")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one 256 MiB copy_kernel before the warmup (the known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE runs)")
@@ -534,7 +539,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, events around every call on the launch stream
+    # per-call times: K eager steps, events around every call on the launch stream
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers]
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -542,7 +547,24 @@ def main():
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_eager = time.perf_counter() - t0
+    elapsed = elapsed_eager
+
+    # timed region: K replays of the whole step captured once as a HIP graph
+    # (the same kernels on the same buffers; no per-launch host gaps)
+    launch = "eager launches"
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        launch = "HIP graph replay of the captured step (per-call times from the eager pass)"
 
     n = len(layers)
     t_cal = np.zeros(n)
@@ -559,6 +581,7 @@ def main():
     t_gemm /= args.steps
 
     ms_per_step = elapsed / args.steps * 1e3
+    ms_per_step_eager = elapsed_eager / args.steps * 1e3
     tot_ops = 0.0
     per = {}
     cal_b = act_b = gemm_ops = 0.0
@@ -627,6 +650,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_eager": round(ms_per_step_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -638,7 +662,8 @@ def main():
                    "act_scale": a_mode, "y_dtype": "bf16",
                    "fused_ffn": ("fc1 GEMM epilogue: ReLU + int8 codes for fc2 (fc2's s and static "
                                  "step); fc2 has no activation quantizer call") if fuse else None,
-                   "step": "sq_calibrate + sq_smooth_quantize_act + sq_gemm_w8a8 per linear"},
+                   "step": "sq_calibrate + sq_smooth_quantize_act + sq_gemm_w8a8 per linear",
+                   "launch": launch},
         "roofline": roof,
         "gemm": {"TOPS": round(gemm_ops / tg / 1e12, 1),
                  "frac": round(gemm_ops / tg / 1e12 / PEAK_INT8_TOPS, 4)},

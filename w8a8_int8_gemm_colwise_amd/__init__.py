@@ -176,15 +176,23 @@ def sq_calibrate(x_cal: torch.Tensor, w: torch.Tensor, alpha: float,
     dev = w.device
     o = dict(out or {})
     f32 = dict(dtype=torch.float32, device=dev)
-    o.setdefault("s", torch.empty(K, **f32))
-    o.setdefault("wq", torch.empty((N, K), dtype=torch.int8, device=dev))
-    o.setdefault("w_scale", torch.empty(N if wm == SQ_W_PER_CHANNEL else 1, **f32))
-    o.setdefault("static_scale", torch.empty(1, **f32))
-    o.setdefault("x_absmax", torch.empty(K, **f32))
-    o.setdefault("w_absmax", torch.empty(K, **f32))
+    if "s" not in o:
+        o["s"] = torch.empty(K, **f32)
+    if "wq" not in o:
+        o["wq"] = torch.empty((N, K), dtype=torch.int8, device=dev)
+    if "w_scale" not in o:
+        o["w_scale"] = torch.empty(N if wm == SQ_W_PER_CHANNEL else 1, **f32)
+    if "static_scale" not in o:
+        o["static_scale"] = torch.empty(1, **f32)
+    if "x_absmax" not in o:
+        o["x_absmax"] = torch.empty(K, **f32)
+    if "w_absmax" not in o:
+        o["w_absmax"] = torch.empty(K, **f32)
     if ln_gamma is not None:
-        o.setdefault("ln_gamma_s", torch.empty(K, **f32))
-        o.setdefault("ln_beta_s", torch.empty(K, **f32))
+        if "ln_gamma_s" not in o:
+            o["ln_gamma_s"] = torch.empty(K, **f32)
+        if "ln_beta_s" not in o:
+            o["ln_beta_s"] = torch.empty(K, **f32)
     _check(lib().sq_calibrate(
         _ptr(x_cal), _dt(x_cal), T, _ptr(w), _dt(w), N, K, float(alpha), wm,
         _ptr(ln_gamma), _ptr(ln_beta), _ptr(o["s"]), _ptr(o["wq"]), _ptr(o["w_scale"]),
@@ -342,15 +350,23 @@ def sq_calibrate_stat(act_stat: torch.Tensor, w: torch.Tensor, alpha: float,
     dev = w.device
     o = dict(out or {})
     f32 = dict(dtype=torch.float32, device=dev)
-    o.setdefault("a", torch.empty(K, **f32))
-    o.setdefault("s", torch.empty(K, **f32))
-    o.setdefault("wq", torch.empty((N, K), dtype=torch.int8, device=dev))
-    o.setdefault("w_scale", torch.empty(N if wm == SQ_W_PER_CHANNEL else 1, **f32))
-    o.setdefault("static_scale", torch.empty(1, **f32))
-    o.setdefault("w_absmax", torch.empty(K, **f32))
+    if "a" not in o:
+        o["a"] = torch.empty(K, **f32)
+    if "s" not in o:
+        o["s"] = torch.empty(K, **f32)
+    if "wq" not in o:
+        o["wq"] = torch.empty((N, K), dtype=torch.int8, device=dev)
+    if "w_scale" not in o:
+        o["w_scale"] = torch.empty(N if wm == SQ_W_PER_CHANNEL else 1, **f32)
+    if "static_scale" not in o:
+        o["static_scale"] = torch.empty(1, **f32)
+    if "w_absmax" not in o:
+        o["w_absmax"] = torch.empty(K, **f32)
     if ln_gamma is not None:
-        o.setdefault("ln_gamma_s", torch.empty(K, **f32))
-        o.setdefault("ln_beta_s", torch.empty(K, **f32))
+        if "ln_gamma_s" not in o:
+            o["ln_gamma_s"] = torch.empty(K, **f32)
+        if "ln_beta_s" not in o:
+            o["ln_beta_s"] = torch.empty(K, **f32)
     _check(lib().sq_calibrate_stat(
         _ptr(act_stat), _ptr(w), _dt(w), N, K, float(alpha), wm, _ptr(ln_gamma), _ptr(ln_beta),
         _ptr(o["s"]), _ptr(o["wq"]), _ptr(o["w_scale"]), _ptr(o["static_scale"]),
