@@ -6,7 +6,7 @@ saturation and weight quantization error) against the oracle:
     65536-token calibration set of the LayerNorm workload on sampled channels;
   * sq_calibrate_stat bit for bit (LayerNorm fold, per-tensor weight step);
   * sq_clip_count exactly (total and per channel) through every quantizer
-    kernel (short rows, cached rows, long rows, LayerNorm);
+    kernel (short rows, cached rows, uncached rows, long rows, LayerNorm);
   * sq_alpha_search within 1e-9 relative (fp64 sums in another order) with the
     same chosen alpha.
 """
@@ -104,9 +104,12 @@ def test_calibrate_stat_matches_oracle(ln, wmode):
 
 
 CLIP = [
-    # M, K, dtype, ln: short rows, cached rows, long rows, LayerNorm
+    # M, K, dtype, ln: short rows, cached rows, uncached rows (4 and 8 chunks per lane),
+    # long rows, LayerNorm
     (300, 128, "bf16", False),
     (97, 4096, "f32", False),
+    (17, 24576, "bf16", False),
+    (9, 40960, "f32", False),
     (33, 65536, "bf16", False),
     (64, 8192, "bf16", True),
     (5, 24576, "f32", True),
