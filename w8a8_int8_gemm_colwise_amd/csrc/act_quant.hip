@@ -11,9 +11,9 @@
 //
 // act_quant_kernel: one token row per block.  The block's lanes own fixed
 // chunks of 8 elements (chunk c = tid + i*blockDim), so per-column data
-// (1/s_k) is computed once per block and reused across the rows the block
-// walks.  The row stays in registers between the absmax reduction and the
-// quantize pass.  Divisions by s_k and by the step use div_rn() (correctly
+// (1/s_k, rcp_rn) is computed once per block and reused across the rows the
+// block walks.  The row stays in registers between the absmax reduction and
+// the quantize pass.  Divisions by s_k and by the step use div_rn() (correctly
 // rounded, five VALU ops).  LayerNorm mode uses exactly 256 lanes so that lane
 // t owns partial t of the canonical fp32 reduction (chunk c -> partial c mod
 // 256, increasing k within a partial, then the fixed halving tree).
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
                 } else {
                     load_chunk(s, c, c0[i]);
 #pragma unroll
-                    for (int e = 0; e < kChunk; ++e) c1[i][e] = 1.0f / c0[i][e];
+                    for (int e = 0; e < kChunk; ++e) c1[i][e] = rcp_rn(c0[i][e]);
                 }
             }
         }
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
                         float sv[kChunk];
                         load_chunk(s, c, sv);
 #pragma unroll
-                        for (int e = 0; e < kChunk; ++e) v[i][e] = div_rn(v[i][e], sv[e], 1.0f / sv[e]);
+                        for (int e = 0; e < kChunk; ++e) v[i][e] = div_rn(v[i][e], sv[e], rcp_rn(sv[e]));
                     }
                 }
             }
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void act_quant_rows_kernel(
     if (act) {
         load_chunk(s, c, c0);
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) c1[e] = 1.0f / c0[e];
+        for (int e = 0; e < kChunk; ++e) c1[e] = rcp_rn(c0[e]);
     } else {
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) c0[e] = c1[e] = 1.0f;
@@ -401,7 +401,7 @@ __device__ __forceinline__ void smooth_chunk(const T* row, int64_t c, const floa
         float sv[kChunk];
         load_chunk(s, c, sv);
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) v[e] = v[e] / sv[e];
+        for (int e = 0; e < kChunk; ++e) v[e] = div_rn(v[e], sv[e], rcp_rn(sv[e]));
     }
 }
 

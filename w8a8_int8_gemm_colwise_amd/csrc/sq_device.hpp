@@ -72,8 +72,24 @@ __device__ __forceinline__ void unpack(const RawChunk<float>& r, float* v) {
     v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
 }
 
+// Correctly rounded reciprocal RN(1/b).  For 2^-126 <= b < 2^126 the
+// hardware estimate r = v_rcp_f32(b) followed by one Newton step in fma,
+// RN(r + r * RN(1 - b*r)), equals the IEEE quotient 1.0f / b: checked on gfx950
+// for every float in that range against the compiler's correctly rounded
+// division (the only mismatches among positive normal b lie at b >= 2^126,
+// where 1/b is subnormal and the estimate flushes it).  Elsewhere (and for
+// b <= 0, NaN) the IEEE division itself.  Three VALU operations and a range
+// test instead of the division sequence.
+__device__ __forceinline__ float rcp_rn(float b) {
+    if (b >= 0x1p-126f && b < 0x1p126f) {
+        const float r = __builtin_amdgcn_rcpf(b);
+        return __builtin_fmaf(__builtin_fmaf(-b, r, 1.0f), r, r);
+    }
+    return 1.0f / b;
+}
+
 // Correctly rounded quotient RN(a / b) for b > 0 normal, given rb = RN(1/b)
-// (computed with an IEEE division).  q0 = RN(a*rb) is within 1.5 ulp of a/b;
+// (rcp_rn or an IEEE division).  q0 = RN(a*rb) is within 1.5 ulp of a/b;
 // one residual step brings it within 1 ulp; by Markstein's theorem (residual
 // r = a - b*q exact, then RN(q + r*rb) with rb within half an ulp of 1/b) the
 // second step returns the correctly rounded quotient.  Valid whenever the
