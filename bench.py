@@ -635,7 +635,7 @@ def main():
     gemm_bytes = sum(_alg(L["spec"], L["M"])[3] for L in layers)
     if tg >= max(tc, ta) and not skinny:
         ach = gemm_ops / tg / 1e12
-        roof = {"kernel": "sq_gemm_w8a8 (gemm_pp_kernel)", "bound": "mfma",
+        roof = {"kernel": "sq_gemm_w8a8 (ping-pong kernels)", "bound": "mfma",
                 "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": _traffic(launches),
                 "launches_per_step": launches, "avg_launch_us": round(tg / launches * 1e6, 2),

@@ -81,12 +81,14 @@ def test_ragged_every_element(case):
     run_layer(spec, xc, w, x, mode, gamma=g, beta=b)
 
 
-@pytest.mark.parametrize("shape", [(1100, 13000, 256), (777, 3000, 1280), (2049, 4097, 512)],
+@pytest.mark.parametrize("shape", [(1100, 13000, 256), (777, 3000, 1280), (2049, 4097, 512),
+                                   (513, 30000, 384), (257, 33000, 384)],
                          ids=lambda t: "x".join(map(str, t)))
 def test_ragged_large_tiles_sampled(shape):
-    """Shapes that select the large-tile kernels with ragged edges in M and N;
-    sampled rows always include the first and last token, sampled columns the
-    first and last output channel."""
+    """Shapes that select the large-tile kernels with ragged edges in M and N
+    (the last two: 256x256 tiles over the first columns and 256x128 tiles over
+    the rest, in one launch); sampled rows always include the first and last
+    token, sampled columns the first and last output channel."""
     M, N, K = shape
     spec = datagen.random_layer(M, N, K, seed=M + N + K, n_outliers=4, T=64)
     xc, w, x = _inputs(spec)

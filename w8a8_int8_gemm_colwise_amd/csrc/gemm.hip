@@ -19,6 +19,9 @@
 //                       waves in two groups alternating memory and compute
 //                       phases ("ping-pong"), three LDS stages filled by
 //                       direct-to-LDS transfers
+//   gemm_pp_mixed_kernel  both ping-pong tiles in one launch: 256x256 over the
+//                       first columns, 256x128 over the rest, when that fills
+//                       the rounds of 256 CUs better than either tile alone
 //   gemm_shortk_kernel  M > 64, K in {64, 128, 256}: the tile's whole K in LDS
 //                       at once, several blocks per CU (store-bound shapes such
 //                       as the attention scores)
@@ -31,6 +34,7 @@
 // int8 codes.  LDS chunks are XOR-swizzled so operand fetches hit distinct
 // banks, and blocks are remapped so that the tiles one XCD runs are neighbours
 // (sharing A rows and B columns in that XCD's L2).
+#include <algorithm>
 #include <type_traits>
 
 #include "sq_device.hpp"
@@ -543,12 +547,20 @@ __device__ __forceinline__ void dma16(const int8_t* base, uint32_t voff, uint32_
 //    before arriving at a barrier);
 //  * every wave waits for its own transfers of stage t+1 before the barrier
 //    that precedes either group's memory phase of stage t+1.
+// LDS bytes of the operand stages of one configuration
+template <int BM, int BN, int BK, int STAGES>
+constexpr int pp_stage_lds() { return STAGES * (BM + BN) * BK; }
+
+// One BM x BN output tile at rows [tm * BM, ...) and columns
+// [n_base + tn * BN, ...), where (tm, tn) is tile `pid` of a tiles_m x tiles_n
+// grid (XCD-aware order).  lds holds the operand stages, scales BM + BN floats
+// and epi_cols 3 * BN floats.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OUT>
-__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
+__device__ __forceinline__ void pp_tile(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
-    int M, int N, int K, Epi epi, Batch bat) {
-    SQ_APPLY_BATCH(OUT);
+    int M, int N, int K, const Epi& epi, int pid, int tiles_m, int tiles_n, int n_base,
+    int8_t* __restrict__ lds, float* __restrict__ scales, float* __restrict__ epi_cols) {
     using T = Tile<BM, BN, WAVES_M, WAVES_N>;
     static_assert(WAVES_M * WAVES_N == 8, "two groups of four waves");
     constexpr int kRows = BM + BN;
@@ -563,15 +575,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     constexpr int kEpiPitch = epi_pitch<OUT, T::TN>();
     static_assert(8 * 32 * kEpiPitch <= STAGES * kStageBytes, "epilogue scratch fits");
     static_assert(BM + BN <= 512, "one scale per thread");
-    __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * kStageBytes];
-    __shared__ __attribute__((aligned(16))) float scales[BM + BN];  // row scales, then column scales
-    __shared__ __attribute__((aligned(16))) float epi_cols[3 * BN];  // bias, s', RN(1/s') per column
-
-    const int tiles_m = (M + BM - 1) / BM;
-    const int tiles_n = (N + BN - 1) / BN;
+    // scales: row scales, then column scales; epi_cols: bias, s', RN(1/s') per column
     int tmi, tni;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tmi, tni);
-    const int m0 = tmi * BM, n0 = tni * BN;
+    tile_coords(pid, tiles_m, tiles_n, tmi, tni);
+    const int m0 = tmi * BM, n0 = n_base + tni * BN;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -698,6 +705,52 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
                                                epi_cols + 2 * BN + cw, epi, D, rD, Y, M, N, scr);
 }
 
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OUT>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
+    int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
+    int M, int N, int K, Epi epi, Batch bat) {
+    SQ_APPLY_BATCH(OUT);
+    __shared__ __attribute__((aligned(1024))) int8_t lds[pp_stage_lds<BM, BN, BK, STAGES>()];
+    __shared__ __attribute__((aligned(16))) float scales[BM + BN];
+    __shared__ __attribute__((aligned(16))) float epi_cols[3 * BN];
+    pp_tile<BM, BN, WAVES_M, WAVES_N, BK, STAGES, OUT>(
+        A, B, sx, sx_per_token, sw, sw_per_tensor, Y, M, N, K, epi, blockIdx.x, (M + BM - 1) / BM,
+        (N + BN - 1) / BN, 0, lds, scales, epi_cols);
+}
+
+// Two tile sizes in one launch: blocks [0, tiles_m * nb_big) take 256x256
+// tiles over the columns [0, 256 * nb_big), the rest 256x128 tiles over the
+// remaining columns.  The large tiles come first, so the last round is made of
+// small ones; shapes whose 256x256 tiles fill whole rounds of the 256 CUs
+// only part of the way use it (launch_gemm's cost model).
+template <int OUT>
+__global__ __launch_bounds__(512, 1) void gemm_pp_mixed_kernel(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
+    int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
+    int M, int N, int K, Epi epi, Batch bat, int nb_big) {
+    SQ_APPLY_BATCH(OUT);
+    constexpr int kLds = pp_stage_lds<256, 256, 64, 3>() > pp_stage_lds<256, 128, 128, 3>()
+                             ? pp_stage_lds<256, 256, 64, 3>()
+                             : pp_stage_lds<256, 128, 128, 3>();
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kLds];
+    __shared__ __attribute__((aligned(16))) float scales[512];
+    __shared__ __attribute__((aligned(16))) float epi_cols[3 * 256];
+    const int tiles_m = (M + 255) / 256;
+    const int big = tiles_m * nb_big;
+    const int pid = blockIdx.x;
+    if (pid < big) {
+        pp_tile<256, 256, 2, 4, 64, 3, OUT>(A, B, sx, sx_per_token, sw, sw_per_tensor, Y, M, N, K,
+                                            epi, pid, tiles_m, nb_big, 0, lds, scales, epi_cols);
+    } else {
+        const int n_base = 256 * nb_big;
+        pp_tile<256, 128, 4, 2, 128, 3, OUT>(A, B, sx, sx_per_token, sw, sw_per_tensor, Y, M, N, K,
+                                             epi, pid - big, tiles_m, (N - n_base + 127) / 128,
+                                             n_base, lds, scales, epi_cols);
+    }
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
 hipError_t run_pp(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
                   const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out, const Epi& epi,
@@ -722,6 +775,31 @@ hipError_t run_pp(const int8_t* xq, const float* sx, bool per_token, const int8_
         default:
             gemm_pp_kernel<BM, BN, WAVES_M, WAVES_N, BK, STAGES, kOutI32>
                 <<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t run_pp_mixed(const int8_t* xq, const float* sx, bool per_token, const int8_t* wq,
+                        const float* sw, bool w_per_tensor, int M, int N, int K, void* y, int out,
+                        const Epi& epi, const Batch& bat, int nb_big, hipStream_t stream) {
+    const int tiles_m = (M + 255) / 256;
+    const int tiles = tiles_m * nb_big + tiles_m * ((N - 256 * nb_big + 127) / 128);
+    const dim3 grid(tiles, static_cast<unsigned>(bat.count)), block(512);
+    const int pt = per_token ? 1 : 0;
+    const int wpt = w_per_tensor ? 1 : 0;
+    switch (out) {
+        case kOutF32:
+            gemm_pp_mixed_kernel<kOutF32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat, nb_big);
+            break;
+        case kOutBF16:
+            gemm_pp_mixed_kernel<kOutBF16><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat, nb_big);
+            break;
+        case kOutI8:
+            gemm_pp_mixed_kernel<kOutI8><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat, nb_big);
+            break;
+        default:
+            gemm_pp_mixed_kernel<kOutI32><<<grid, block, 0, stream>>>(xq, wq, sx, pt, sw, wpt, y, M, N, K, epi, bat, nb_big);
             break;
     }
     return hipGetLastError();
@@ -1085,17 +1163,30 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
     // tile, operand offsets in int32
     const bool pp_ok = (K % 128 == 0) && M * K < (int64_t(1) << 31) && N * K < (int64_t(1) << 31);
     if (pp_ok) {
-        // pick the tile by whole rounds of 256 CUs: a 256x256 tile does twice
-        // the work of a 256x128 tile at slightly higher efficiency
-        const int64_t t_big = ((M + 255) / 256) * ((N + 255) / 256);
-        const int64_t t_mid = ((M + 255) / 256) * ((N + 127) / 128);
-        const int64_t cost_big = ((t_big + 255) / 256) * 2 * 100;
-        const int64_t cost_mid = ((t_mid + 255) / 256) * 105;
-        if (cost_big <= cost_mid)
+        // pick the tiles by whole rounds of 256 CUs: a round of 256x256 tiles
+        // (twice the work of a 256x128 tile) takes about 180/105 of a round of
+        // 256x128 tiles (measured at K = 4096).  The first nb 256-column
+        // blocks may take 256x256 tiles and the rest 256x128 tiles, in one
+        // launch, large ones first.
+        const int64_t tm = ((M + 255) / 256) * bat.count;  // row tiles of every batch entry
+        const int64_t nb_all = (N + 255) / 256;
+        int64_t best_nb = 0, best_cost = -1;
+        for (int64_t nb = 0; nb <= nb_all; ++nb) {
+            const int64_t rest = std::max<int64_t>(0, N - 256 * nb);
+            const int64_t cost = ((tm * nb + 255) / 256) * 180 + ((tm * ((rest + 127) / 128) + 255) / 256) * 105;
+            if (best_cost < 0 || cost < best_cost || (cost == best_cost && nb == nb_all)) {
+                best_cost = cost;
+                best_nb = nb;
+            }
+        }
+        if (best_nb == nb_all)
             return run_pp<256, 256, 2, 4, 64, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
                                                  out_kind, epi, bat, stream);
-        return run_pp<256, 128, 4, 2, 128, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
-                                              out_kind, epi, bat, stream);
+        if (best_nb == 0)
+            return run_pp<256, 128, 4, 2, 128, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
+                                                  out_kind, epi, bat, stream);
+        return run_pp_mixed(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y, out_kind, epi, bat,
+                            static_cast<int>(best_nb), stream);
     }
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 127) / 128);
     if (big_tiles >= 256)

@@ -17,7 +17,7 @@ import glob
 import json
 import os
 
-GEMM_KERNELS = ("gemm_pp_kernel", "gemm_shortk_kernel", "gemm_skinny_kernel", "gemm_kernel")
+GEMM_KERNELS = ("gemm_pp_kernel", "gemm_pp_mixed_kernel", "gemm_shortk_kernel", "gemm_skinny_kernel", "gemm_kernel")
 
 
 def short(name: str) -> str:

@@ -30,7 +30,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 GEMM_SRC = os.path.join(HERE, "csrc", "gemm.hip")
 COPY_BYTES = 256 << 20
-GEMM_KERNELS = ("gemm_pp_kernel", "gemm_shortk_kernel", "gemm_skinny_kernel", "gemm_kernel")
+GEMM_KERNELS = ("gemm_pp_kernel", "gemm_pp_mixed_kernel", "gemm_shortk_kernel", "gemm_skinny_kernel", "gemm_kernel")
 
 
 def _dispatches(d: str, counter: str):
