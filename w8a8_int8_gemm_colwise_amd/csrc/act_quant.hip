@@ -67,6 +67,28 @@ __device__ __forceinline__ float canonical_tree(float p, float* lds) {
     return r;
 }
 
+// RN(1/s) of a chunk's eight column factors (rcp_rn), with the range test taken
+// once for the chunk: the short sequence when every factor lies in
+// [2^-126, 2^126), the IEEE division otherwise.
+__device__ __forceinline__ void rcp_chunk(const float (&sv)[kChunk], float (&rs)[kChunk]) {
+    float lo = sv[0], hi = sv[0];
+#pragma unroll
+    for (int e = 1; e < kChunk; ++e) {
+        lo = fminf(lo, sv[e]);
+        hi = fmaxf(hi, sv[e]);
+    }
+    if (lo >= 0x1p-126f && hi < 0x1p126f) {
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+            const float r = __builtin_amdgcn_rcpf(sv[e]);
+            rs[e] = __builtin_fmaf(__builtin_fmaf(-sv[e], r, 1.0f), r, r);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) rs[e] = 1.0f / sv[e];
+    }
+}
+
 // Quantize one smoothed value with step d (rd = RN(1/d)).  In static mode the
 // dividend is first limited to +-128 d (exact scaling by a power of two), which
 // keeps the quotient finite and leaves every code unchanged: a quotient beyond
@@ -118,7 +140,7 @@ __device__ __forceinline__ void flush_clips(int n, unsigned long long* clip) {
 // rowmax != nullptr (dynamic modes only): the row pass that stores the raw
 // maximum max_k |xh_k| of every row in rowmax[m] and writes neither codes nor
 // x_scale -- the first pass of the dynamic per-tensor step.
-template <typename T, bool LN, bool STATIC, int CPT, int D, int MAXT>
+template <typename T, bool LN, bool STATIC, int CPT, int D, int MAXT, bool CACHE_ = (D > 0)>
 __global__ __launch_bounds__(MAXT) void act_quant_kernel(
     const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
     const float* __restrict__ gs, const float* __restrict__ bs, float eps,
@@ -130,7 +152,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
     const int nthr = blockDim.x;
     const int64_t chunks = K / kChunk;
     const float kf = static_cast<float>(K);
-    constexpr bool CACHE = D > 0;
+    constexpr bool CACHE = CACHE_;
     constexpr int CC = CACHE ? CPT : 1;
     const int64_t G = gridDim.x;
 
@@ -241,8 +263,12 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
                     } else {
                         float sv[kChunk];
                         load_chunk(s, c, sv);
+                        {
+                            float rs[kChunk];
+                            rcp_chunk(sv, rs);
 #pragma unroll
-                        for (int e = 0; e < kChunk; ++e) v[i][e] = div_rn(v[i][e], sv[e], rcp_rn(sv[e]));
+                            for (int e = 0; e < kChunk; ++e) v[i][e] = div_rn(v[i][e], sv[e], rs[e]);
+                        }
                     }
                 }
             }
@@ -400,8 +426,12 @@ __device__ __forceinline__ void smooth_chunk(const T* row, int64_t c, const floa
     } else {
         float sv[kChunk];
         load_chunk(s, c, sv);
+        {
+            float rs[kChunk];
+            rcp_chunk(sv, rs);
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) v[e] = div_rn(v[e], sv[e], rcp_rn(sv[e]));
+            for (int e = 0; e < kChunk; ++e) v[e] = div_rn(v[e], sv[e], rs[e]);
+        }
     }
 }
 
