@@ -1170,8 +1170,11 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
         // launch, large ones first.
         const int64_t tm = ((M + 255) / 256) * bat.count;  // row tiles of every batch entry
         const int64_t nb_all = (N + 255) / 256;
+        // with r rounds of large tiles the best split is the widest that fits
+        const int64_t rounds_all = (tm * nb_all + 255) / 256;
         int64_t best_nb = 0, best_cost = -1;
-        for (int64_t nb = 0; nb <= nb_all; ++nb) {
+        for (int64_t r = 0; r <= rounds_all; ++r) {
+            const int64_t nb = std::min<int64_t>(nb_all, 256 * r / tm);
             const int64_t rest = std::max<int64_t>(0, N - 256 * nb);
             const int64_t cost = ((tm * nb + 255) / 256) * 180 + ((tm * ((rest + 127) / 128) + 255) / 256) * 105;
             if (best_cost < 0 || cost < best_cost || (cost == best_cost && nb == nb_all)) {
