@@ -142,6 +142,27 @@ def _dev2d(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be a contiguous 2-D tensor")
 
 
+def _vec(t: torch.Tensor | None, n, name: str, device, dtype=torch.float32):
+    """A caller-supplied vector (input or output): contiguous, on ``device``, of
+    ``dtype`` and with exactly ``n`` elements (or one of the counts in ``n``)."""
+    if t is None:
+        return
+    counts = n if isinstance(n, tuple) else (n,)
+    if (not t.is_cuda or t.device != device or t.dtype != dtype or not t.is_contiguous()
+            or t.numel() not in counts):
+        want = " or ".join(str(c) for c in counts)
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of {want} elements "
+                         f"on {device}")
+
+
+def _out2d(t: torch.Tensor, rows: int, cols: int, name: str, device, dtype):
+    """A caller-supplied 2-D output: contiguous [rows, cols] of ``dtype`` on ``device``."""
+    if (not t.is_cuda or t.device != device or t.dtype != dtype or not t.is_contiguous()
+            or tuple(t.shape) != (rows, cols)):
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of shape "
+                         f"[{rows}, {cols}] on {device}")
+
+
 def _mode(mode) -> int:
     if mode in ("per_token", SQ_PER_TOKEN):
         return SQ_PER_TOKEN
@@ -174,25 +195,25 @@ def sq_calibrate(x_cal: torch.Tensor, w: torch.Tensor, alpha: float,
     if K != K2:
         raise ValueError("x_cal and w disagree on K")
     dev = w.device
+    if x_cal.device != dev:
+        raise ValueError("x_cal and w must be on one device")
+    _vec(ln_gamma, K, "ln_gamma", dev)
+    _vec(ln_beta, K, "ln_beta", dev)
     o = dict(out or {})
     f32 = dict(dtype=torch.float32, device=dev)
-    if "s" not in o:
-        o["s"] = torch.empty(K, **f32)
-    if "wq" not in o:
-        o["wq"] = torch.empty((N, K), dtype=torch.int8, device=dev)
-    if "w_scale" not in o:
-        o["w_scale"] = torch.empty(N if wm == SQ_W_PER_CHANNEL else 1, **f32)
-    if "static_scale" not in o:
-        o["static_scale"] = torch.empty(1, **f32)
-    if "x_absmax" not in o:
-        o["x_absmax"] = torch.empty(K, **f32)
-    if "w_absmax" not in o:
-        o["w_absmax"] = torch.empty(K, **f32)
+    nws = N if wm == SQ_W_PER_CHANNEL else 1
+    vecs = {"s": K, "w_scale": nws, "static_scale": 1, "x_absmax": K, "w_absmax": K}
     if ln_gamma is not None:
-        if "ln_gamma_s" not in o:
-            o["ln_gamma_s"] = torch.empty(K, **f32)
-        if "ln_beta_s" not in o:
-            o["ln_beta_s"] = torch.empty(K, **f32)
+        vecs.update(ln_gamma_s=K, ln_beta_s=K)
+    for k, n in vecs.items():
+        if k in o:
+            _vec(o[k], n, f"out[{k!r}]", dev)
+        else:
+            o[k] = torch.empty(n, **f32)
+    if "wq" in o:
+        _out2d(o["wq"], N, K, "out['wq']", dev, torch.int8)
+    else:
+        o["wq"] = torch.empty((N, K), dtype=torch.int8, device=dev)
     _check(lib().sq_calibrate(
         _ptr(x_cal), _dt(x_cal), T, _ptr(w), _dt(w), N, K, float(alpha), wm,
         _ptr(ln_gamma), _ptr(ln_beta), _ptr(o["s"]), _ptr(o["wq"]), _ptr(o["w_scale"]),
@@ -212,11 +233,22 @@ def sq_smooth_quantize_act(x: torch.Tensor, s: torch.Tensor | None = None,
     _dev2d(x, "x")
     M, K = x.shape
     md = _mode(mode)
+    dev = x.device
+    _vec(s, K, "s", dev)
+    _vec(ln_gamma_s, K, "ln_gamma_s", dev)
+    _vec(ln_beta_s, K, "ln_beta_s", dev)
+    if md == SQ_STATIC_PER_TENSOR:
+        _vec(static_scale, 1, "static_scale", dev)
     if xq is None:
-        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    if md != SQ_STATIC_PER_TENSOR and x_scale is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    else:
+        _out2d(xq, M, K, "xq", dev, torch.int8)
+    if md != SQ_STATIC_PER_TENSOR:
         n = M if md == SQ_PER_TOKEN else 1
-        x_scale = torch.empty(n, dtype=torch.float32, device=x.device)
+        if x_scale is None:
+            x_scale = torch.empty(n, dtype=torch.float32, device=dev)
+        else:
+            _vec(x_scale, n, "x_scale", dev)
     _check(lib().sq_smooth_quantize_act(
         _ptr(x), _dt(x), M, K, _ptr(s), _ptr(ln_gamma_s), _ptr(ln_beta_s), float(ln_eps), md,
         _ptr(static_scale) if md == SQ_STATIC_PER_TENSOR else None, _ptr(xq),
@@ -228,22 +260,37 @@ _OUT = {"f32": (SQ_F32, torch.float32), "bf16": (SQ_BF16, torch.bfloat16),
         "i32": (SQ_I32, torch.int32), "i8": (SQ_I8, torch.int8)}
 
 
-def sq_gemm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor,
-                 w_scale: torch.Tensor | None, mode="per_token", out_dtype: str = "bf16",
-                 y: torch.Tensor | None = None, w_mode="per_channel") -> torch.Tensor:
-    """Int8 GEMM + dequant: y[M,N] = RN(float(acc) * RN(dx_t * dw_n)); mode is
-    the activation step granularity, w_mode the weight's."""
+def _gemm_args(xq, x_scale, wq, w_scale, md, wm, code, tdt, y):
+    """Shapes of a GEMM call; checks the scales and a caller-supplied output."""
     _dev2d(xq, "xq")
     _dev2d(wq, "wq")
     M, K = xq.shape
     N, K2 = wq.shape
     if K != K2:
         raise ValueError("xq and wq disagree on K")
-    code, tdt = _OUT[out_dtype]
+    dev = xq.device
+    if wq.device != dev:
+        raise ValueError("xq and wq must be on one device")
+    if code != SQ_I32:
+        _vec(x_scale, M if md == SQ_PER_TOKEN else 1, "x_scale", dev)
+        _vec(w_scale, N if wm == SQ_W_PER_CHANNEL else 1, "w_scale", dev)
     if y is None:
-        y = torch.empty((M, N), dtype=tdt, device=xq.device)
-    _check(lib().sq_gemm_w8a8(_ptr(xq), _ptr(x_scale), _mode(mode), _ptr(wq), _ptr(w_scale),
-                              _wmode(w_mode), M, N, K, _ptr(y), code, _stream(xq.device)))
+        y = torch.empty((M, N), dtype=tdt, device=dev)
+    else:
+        _out2d(y, M, N, "y", dev, tdt)
+    return M, N, K, y
+
+
+def sq_gemm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor,
+                 w_scale: torch.Tensor | None, mode="per_token", out_dtype: str = "bf16",
+                 y: torch.Tensor | None = None, w_mode="per_channel") -> torch.Tensor:
+    """Int8 GEMM + dequant: y[M,N] = RN(float(acc) * RN(dx_t * dw_n)); mode is
+    the activation step granularity, w_mode the weight's."""
+    code, tdt = _OUT[out_dtype]
+    md, wm = _mode(mode), _wmode(w_mode)
+    M, N, K, y = _gemm_args(xq, x_scale, wq, w_scale, md, wm, code, tdt, y)
+    _check(lib().sq_gemm_w8a8(_ptr(xq), _ptr(x_scale), md, _ptr(wq), _ptr(w_scale),
+                              wm, M, N, K, _ptr(y), code, _stream(xq.device)))
     return y
 
 
@@ -256,18 +303,15 @@ def sq_gemm_w8a8_ex(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Te
     """Int8 GEMM with the fused epilogue: dequantize, + bias, ReLU, then fp32 /
     bf16 output, or (out_dtype "i8") the next linear's int8 codes for its
     smoothing factor next_s and static step next_scale [1]."""
-    _dev2d(xq, "xq")
-    _dev2d(wq, "wq")
-    M, K = xq.shape
-    N, K2 = wq.shape
-    if K != K2:
-        raise ValueError("xq and wq disagree on K")
     code, tdt = _OUT[out_dtype]
-    if y is None:
-        y = torch.empty((M, N), dtype=tdt, device=xq.device)
+    md, wm = _mode(mode), _wmode(w_mode)
+    M, N, K, y = _gemm_args(xq, x_scale, wq, w_scale, md, wm, code, tdt, y)
+    _vec(bias, N, "bias", xq.device)
+    _vec(next_s, N, "next_s", xq.device)
+    _vec(next_scale, 1, "next_scale", xq.device)
     epi = SqEpilogue(_ptr(bias), _ptr(next_s), _ptr(next_scale), int(bool(relu)))
-    _check(lib().sq_gemm_w8a8_ex(_ptr(xq), _ptr(x_scale), _mode(mode), _ptr(wq), _ptr(w_scale),
-                                 _wmode(w_mode), M, N, K, ctypes.byref(epi), _ptr(y), code,
+    _check(lib().sq_gemm_w8a8_ex(_ptr(xq), _ptr(x_scale), md, _ptr(wq), _ptr(w_scale),
+                                 wm, M, N, K, ctypes.byref(epi), _ptr(y), code,
                                  _stream(xq.device)))
     return y
 
@@ -304,8 +348,13 @@ def sq_bmm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor | None, wq: torch.Tensor
         y = torch.empty((B, M, N), dtype=tdt, device=xq.device)
     elif y.dtype != tdt or not y.is_cuda or not y.is_contiguous() or y.numel() != B * M * N:
         raise ValueError(f"y must be a contiguous GPU tensor of {B}x{M}x{N} {tdt}")
+    if wq.device != xq.device or y.device != xq.device:
+        raise ValueError("xq, wq and y must be on one device")
     xs_n = M if md == SQ_PER_TOKEN else 1
     ws_n = N if wm == SQ_W_PER_CHANNEL else 1
+    if code != SQ_I32:
+        _vec(x_scale, (xs_n, B * xs_n), "x_scale", xq.device)
+        _vec(w_scale, (ws_n, B * ws_n), "w_scale", xq.device)
     _check(lib().sq_bmm_w8a8(
         _ptr(xq), 0 if xq.dim() == 2 else M * K, _ptr(x_scale), _stride(x_scale, xs_n), md,
         _ptr(wq), 0 if wq.dim() == 2 else N * K, _ptr(w_scale), _stride(w_scale, ws_n), wm,
@@ -332,6 +381,8 @@ def sq_channel_quantile(x: torch.Tensor, q: float, out: torch.Tensor | None = No
     ws = _workspace(nb, x.device, workspace)
     if out is None:
         out = torch.empty(K, dtype=torch.float32, device=x.device)
+    else:
+        _vec(out, K, "out", x.device)
     _check(lib().sq_channel_quantile(_ptr(x), _dt(x), T, K, float(q), _ptr(out), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(x.device)))
     return out
@@ -345,28 +396,27 @@ def sq_calibrate_stat(act_stat: torch.Tensor, w: torch.Tensor, alpha: float,
     wm = _wmode(w_mode)
     _dev2d(w, "w")
     N, K = w.shape
-    if act_stat.dim() != 1 or act_stat.numel() != K or act_stat.dtype != torch.float32:
-        raise ValueError("act_stat must be a float32 [K] tensor")
     dev = w.device
+    if act_stat.dim() != 1:
+        raise ValueError("act_stat must be a float32 [K] tensor")
+    _vec(act_stat, K, "act_stat", dev)
+    _vec(ln_gamma, K, "ln_gamma", dev)
+    _vec(ln_beta, K, "ln_beta", dev)
     o = dict(out or {})
     f32 = dict(dtype=torch.float32, device=dev)
-    if "a" not in o:
-        o["a"] = torch.empty(K, **f32)
-    if "s" not in o:
-        o["s"] = torch.empty(K, **f32)
-    if "wq" not in o:
-        o["wq"] = torch.empty((N, K), dtype=torch.int8, device=dev)
-    if "w_scale" not in o:
-        o["w_scale"] = torch.empty(N if wm == SQ_W_PER_CHANNEL else 1, **f32)
-    if "static_scale" not in o:
-        o["static_scale"] = torch.empty(1, **f32)
-    if "w_absmax" not in o:
-        o["w_absmax"] = torch.empty(K, **f32)
+    nws = N if wm == SQ_W_PER_CHANNEL else 1
+    vecs = {"a": K, "s": K, "w_scale": nws, "static_scale": 1, "w_absmax": K}
     if ln_gamma is not None:
-        if "ln_gamma_s" not in o:
-            o["ln_gamma_s"] = torch.empty(K, **f32)
-        if "ln_beta_s" not in o:
-            o["ln_beta_s"] = torch.empty(K, **f32)
+        vecs.update(ln_gamma_s=K, ln_beta_s=K)
+    for k, n in vecs.items():
+        if k in o:
+            _vec(o[k], n, f"out[{k!r}]", dev)
+        else:
+            o[k] = torch.empty(n, **f32)
+    if "wq" in o:
+        _out2d(o["wq"], N, K, "out['wq']", dev, torch.int8)
+    else:
+        o["wq"] = torch.empty((N, K), dtype=torch.int8, device=dev)
     _check(lib().sq_calibrate_stat(
         _ptr(act_stat), _ptr(w), _dt(w), N, K, float(alpha), wm, _ptr(ln_gamma), _ptr(ln_beta),
         _ptr(o["s"]), _ptr(o["wq"]), _ptr(o["w_scale"]), _ptr(o["static_scale"]),
@@ -382,6 +432,10 @@ def sq_clip_count(x: torch.Tensor, static_scale: torch.Tensor, s: torch.Tensor |
     int32 [K] or None)."""
     _dev2d(x, "x")
     M, K = x.shape
+    _vec(static_scale, 1, "static_scale", x.device)
+    _vec(s, K, "s", x.device)
+    _vec(ln_gamma_s, K, "ln_gamma_s", x.device)
+    _vec(ln_beta_s, K, "ln_beta_s", x.device)
     count = torch.empty(1, dtype=torch.int64, device=x.device)
     pc = torch.empty(K, dtype=torch.int32, device=x.device) if per_channel else None
     _check(lib().sq_clip_count(_ptr(x), _dt(x), M, K, _ptr(s), _ptr(ln_gamma_s), _ptr(ln_beta_s),
@@ -399,6 +453,8 @@ def sq_alpha_search(x_cal: torch.Tensor, w: torch.Tensor, alphas, mode="per_toke
     N, K2 = w.shape
     if K != K2:
         raise ValueError("x_cal and w disagree on K")
+    if x_cal.device != w.device:
+        raise ValueError("x_cal and w must be on one device")
     al = (ctypes.c_float * len(alphas))(*[float(a) for a in alphas])
     nb = lib().sq_alpha_search_workspace_size(T, N, K)
     ws = _workspace(nb, w.device, workspace)
