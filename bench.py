@@ -73,40 +73,95 @@ def _traffic(gemm_launches: int):
         return None
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(workload, max_tokens: int = 256, w_mode: str = "per_channel",
-                 a_mode: str = "per_token"):
+                 a_mode: str = "per_token", single_tokens: int = 32):
     """Time the CPU oracle on a bounded sample of the workload: every linear's
     full calibration and weight quantization, then activation quantization,
-    int8 GEMM and dequant for the first ``max_tokens`` tokens."""
+    int8 GEMM and dequant for the first ``max_tokens`` tokens, each phase timed
+    on its own; then the first linear again on one thread with
+    ``single_tokens`` tokens."""
     import datagen
     import oracle
 
-    ops = 0.0
-    t_total = 0.0
     wpt = w_mode == "per_tensor"
-    for spec in workload.layers:
+
+    def run_linear(spec, tokens, phases):
         xc, w = datagen.calibration_x(spec), datagen.weights(spec)
-        x = datagen.eval_x(spec)[:max_tokens]
+        x = datagen.eval_x(spec)[:tokens]
         g = b = None
         if spec.ln:
             g, b = datagen.ln_params(spec)
         t0 = time.perf_counter()
         cal = oracle.calibrate(xc, w, spec.alpha, g, b, w_per_tensor=wpt)
+        t1 = time.perf_counter()
         kw = dict(g_s=cal["g_s"], b_s=cal["b_s"]) if spec.ln else dict(s=cal["s"])
         xq, xs, _ = oracle.smooth_quantize_act(
             x, static=cal["static_scale"] if a_mode == "static" else None,
             dynamic_per_tensor=a_mode == "dynamic_per_tensor", **kw)
+        t2 = time.perf_counter()
         y = oracle.gemm_w8a8(xq, xs, cal["wq"], cal["w_scale"], per_token=a_mode == "per_token",
                              out="bf16", w_per_tensor=wpt)
-        t_total += time.perf_counter() - t0
-        ops += 2.0 * x.shape[0] * spec.N * spec.K
+        t3 = time.perf_counter()
         del y
-    return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
+        phases["calibrate"] += t1 - t0
+        phases["act_quant"] += t2 - t1
+        phases["gemm"] += t3 - t2
+        return 2.0 * x.shape[0] * spec.N * spec.K
+
+    phases = dict(calibrate=0.0, act_quant=0.0, gemm=0.0)
+    ops = sum(run_linear(spec, max_tokens, phases) for spec in workload.layers)
+    t_total = sum(phases.values())
+    threads = oracle.num_threads()
+    one = dict(calibrate=0.0, act_quant=0.0, gemm=0.0)
+    oracle.set_num_threads(1)
+    try:
+        ops1 = run_linear(workload.layers[0], single_tokens, one)
+    finally:
+        oracle.set_num_threads(threads)
+    t1 = sum(one.values())
+    name0 = workload.layers[0].name
+    return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": threads,
             "kind": "oracle",
             "sample": (f"every linear: full calibration + weight quantization, then activation "
                        f"quantization + int8 GEMM + bf16 dequant of {max_tokens} of "
                        f"{workload.layers[0].M} tokens; value = GEMM ops of the sample / "
-                       f"oracle wall time ({t_total:.1f} s)")}
+                       f"oracle wall time ({t_total:.1f} s)"),
+            "phases_s": {k: round(v, 3) for k, v in phases.items()},
+            "single_thread": {"value": ops1 / t1 / 1e12, "unit": "TOPS", "cores": 1,
+                              "sample": (f"linear {name0}: full calibration, then {single_tokens} "
+                                         f"tokens ({t1:.1f} s)"),
+                              "phases_s": {k: round(v, 3) for k, v in one.items()}},
+            "host": {"nproc": os.cpu_count(), "cpu_model": _cpu_model()}}
+
+
+def cpu_baseline_quantile(xc_host, q: float, cols: int):
+    """Time the CPU oracle's channel quantile on the first ``cols`` channels of
+    the calibration set (every token)."""
+    import oracle
+
+    T, K = xc_host.shape
+    cols = max(1, min(cols, K))
+    sub = np.ascontiguousarray(xc_host[:, :cols])
+    t0 = time.perf_counter()
+    oracle.channel_quantile(sub, q)
+    t = time.perf_counter() - t0
+    return {"value": T * cols * sub.itemsize / t / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"q = {q} nearest-rank quantile of |x| for {cols} of {K} channels over "
+                       f"all {T} calibration tokens (numpy sort, one thread); value = sample "
+                       f"bytes / oracle wall time ({t:.1f} s)"),
+            "host": {"nproc": os.cpu_count(), "cpu_model": _cpu_model()}}
 
 
 def _attn_inputs(H, S, D):
@@ -148,7 +203,8 @@ def cpu_baseline_attention(heads: int):
             "kind": "oracle",
             "sample": (f"{heads} of {H} heads: per-token quantization of Q, K, P, V^T rows, "
                        f"S = Q K^T and O = P V with bf16 outputs; value = BMM ops of the sample "
-                       f"/ oracle wall time ({t:.1f} s)")}
+                       f"/ oracle wall time ({t:.1f} s)"),
+            "host": {"nproc": os.cpu_count(), "cpu_model": _cpu_model()}}
 
 
 def bench_attention(args, attain_fn):
@@ -302,7 +358,8 @@ def bench_robust(args, attain_fn):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
     spec = datagen.workload(5).layers[0]
-    xc = bf(datagen.calibration_x(spec))
+    xc_host = datagen.calibration_x(spec)
+    xc = bf(xc_host)
     w = bf(datagen.weights(spec))
     x = bf(datagen.eval_x(spec))
     g, b = (torch.from_numpy(t).to(dev) for t in datagen.ln_params(spec))
@@ -401,6 +458,8 @@ def bench_robust(args, attain_fn):
     }
     if attain:
         out["attainable"] = attain
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_quantile(xc_host, 0.999, args.cpu_cols)
     return out
 
 
@@ -429,6 +488,8 @@ def main():
                          "per token (default); O1-O3 = the per-tensor weight settings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-cols", type=int, default=2048,
+                    help="robust workload: channels of the CPU oracle's quantile sample")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="attn6.7b: heads of the CPU oracle's sample")
     ap.add_argument("--fuse-ffn", action="store_true",

@@ -78,6 +78,8 @@ def lib():
         L.orc_f32_to_bf16.argtypes = [f32p, i64, vp]
         L.orc_ln_f64.argtypes = [vp, ci, i64, i64, vp, vp, ctypes.c_double, vp]
         L.orc_num_threads.restype = ci
+        L.orc_set_num_threads.argtypes = [ci]
+        L.orc_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -110,6 +112,10 @@ def _rows(rows):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
 
 
 # ---- the path ----------------------------------------------------------------

@@ -54,6 +54,9 @@ static float step_from_absmax(float m) {
 
 int orc_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads of the OpenMP loops (the benchmark also times one thread). */
+void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* ---- calibration -------------------------------------------------------- */
 
 /* [Teach] §四 and [Edge] §三: calibration records the absolute peak of every
