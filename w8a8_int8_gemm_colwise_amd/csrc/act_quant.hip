@@ -14,9 +14,10 @@
 // (1/s_k, rcp_rn) is computed once per block and reused across the rows the
 // block walks.  The row stays in registers between the absmax reduction and
 // the quantize pass.  Divisions by s_k and by the step use div_rn() (correctly
-// rounded, five VALU ops).  LayerNorm mode uses exactly 256 lanes so that lane
-// t owns partial t of the canonical fp32 reduction (chunk c -> partial c mod
-// 256, increasing k within a partial, then the fixed halving tree).
+// rounded, five VALU ops; three for x / s_k when x is bf16, div_x).  LayerNorm
+// mode uses exactly 256 lanes so that lane t owns partial t of the canonical
+// fp32 reduction (chunk c -> partial c mod 256, increasing k within a partial,
+// then the fixed halving tree).
 // act_quant_rows_kernel packs several short rows (K <= 256) into a wave;
 // act_quant_stream_kernel re-reads long rows per sweep.  All three share the
 // per-element arithmetic and have a row-maximum pass (the first pass of the
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
                     if (CACHE) {
 #pragma unroll
                         for (int e = 0; e < kChunk; ++e)
-                            v[i][e] = div_rn(v[i][e], c0[CACHE ? i : 0][e], c1[CACHE ? i : 0][e]);
+                            v[i][e] = div_x<T>(v[i][e], c0[CACHE ? i : 0][e], c1[CACHE ? i : 0][e]);
                     } else {
                         float sv[kChunk];
                         load_chunk(s, c, sv);
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
                             float rs[kChunk];
                             rcp_chunk(sv, rs);
 #pragma unroll
-                            for (int e = 0; e < kChunk; ++e) v[i][e] = div_rn(v[i][e], sv[e], rs[e]);
+                            for (int e = 0; e < kChunk; ++e) v[i][e] = div_x<T>(v[i][e], sv[e], rs[e]);
                         }
                     }
                 }
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(256) void act_quant_rows_kernel(
         float v[kChunk];
         unpack(cur, v);
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) v[e] = div_rn(v[e], c0[e], c1[e]);
+        for (int e = 0; e < kChunk; ++e) v[e] = div_x<T>(v[e], c0[e], c1[e]);
         float d, rd;
         if (STATIC) {
             d = d_static;
@@ -430,7 +431,7 @@ __device__ __forceinline__ void smooth_chunk(const T* row, int64_t c, const floa
             float rs[kChunk];
             rcp_chunk(sv, rs);
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) v[e] = div_rn(v[e], sv[e], rs[e]);
+            for (int e = 0; e < kChunk; ++e) v[e] = div_x<T>(v[e], sv[e], rs[e]);
         }
     }
 }

@@ -105,6 +105,27 @@ __device__ __forceinline__ float div_rn(float a, float b, float rb) {
     return __builtin_fmaf(r, rb, q);
 }
 
+// RN(a / b) as div_rn when a has at most 8 significant bits (a bf16 value):
+// then q0 = RN(a*rb) is always within one ulp of a/b and the first residual
+// step already returns the correctly rounded quotient.  Checked on gfx950
+// against the IEEE division for every bf16 significand of a and every fp32
+// significand of b, with quotients in [0.5, 2) (2^31 pairs); scaling a and b
+// by powers of two does not change the rounding, and the same validity range
+// as div_rn applies.  Three VALU operations.
+__device__ __forceinline__ float div_rn_narrow(float a, float b, float rb) {
+    const float q = a * rb;
+    const float r = __builtin_fmaf(-b, q, a);
+    return __builtin_fmaf(r, rb, q);
+}
+
+// x / s for an activation element of storage type T: bf16 values have 8
+// significant bits, so the short sequence is exact for them.
+template <typename T>
+__device__ __forceinline__ float div_x(float x, float s, float rs) {
+    if constexpr (sizeof(T) == 2) return div_rn_narrow(x, s, rs);
+    else return div_rn(x, s, rs);
+}
+
 // Quantizer step from an absolute maximum: RN(max(FLOOR, m) / 127).
 __device__ __forceinline__ float step_from_absmax(float m) {
     return fmaxf(m, kFloor) / kQmax;
