@@ -50,15 +50,16 @@ template <> struct Mag<float> {
 constexpr int kQCols = 64;       // columns per block, one per lane
 constexpr int kQThreads = 512;   // 8 waves walk interleaved rows
 constexpr int kQBins = 256;
-constexpr int kQPitch = 257;     // padded LDS row: equal bins of different columns in different banks
-constexpr int kQUnroll = 4;
+constexpr int kQUnroll = 16;     // loads in flight per lane (2 or 4 bytes each)
 
 template <typename T>
 __global__ __launch_bounds__(kQThreads) void quantile_hist_kernel(
     const T* __restrict__ x, int64_t rows, int64_t K, int64_t rpb, int shift, int width,
     const uint32_t* __restrict__ prefix, uint32_t* __restrict__ hist) {
-    __shared__ uint32_t h[kQCols * kQPitch];
-    for (int i = threadIdx.x; i < kQCols * kQPitch; i += kQThreads) h[i] = 0u;
+    // bin-major: h[bin * 64 + lane], so a lane's counters all sit in its own
+    // bank and a wave's 64 increments never collide, whatever the bins
+    __shared__ uint32_t h[kQBins * kQCols];
+    for (int i = threadIdx.x; i < kQBins * kQCols; i += kQThreads) h[i] = 0u;
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kQThreads) void quantile_hist_kernel(
     const int64_t r1 = std::min<int64_t>(rows, r0 + rpb);
     if (col < K) {
         const uint32_t pre = prefix[col];
-        uint32_t* hl = h + lane * kQPitch;
+        uint32_t* hl = h + lane;
         constexpr int kStride = kQThreads / 64;
         int64_t t = r0 + wave;
         for (; t + (kQUnroll - 1) * kStride < r1; t += kQUnroll * kStride) {
@@ -79,19 +80,19 @@ __global__ __launch_bounds__(kQThreads) void quantile_hist_kernel(
 #pragma unroll
             for (int u = 0; u < kQUnroll; ++u) {
                 const uint32_t m = Mag<T>::of(v[u]);
-                if ((m >> hi) == pre) atomicAdd(hl + ((m >> shift) & mask), 1u);
+                if ((m >> hi) == pre) atomicAdd(hl + ((m >> shift) & mask) * kQCols, 1u);
             }
         }
         for (; t < r1; t += kStride) {
             const uint32_t m = Mag<T>::of(x[t * K + col]);
-            if ((m >> hi) == pre) atomicAdd(hl + ((m >> shift) & mask), 1u);
+            if ((m >> hi) == pre) atomicAdd(hl + ((m >> shift) & mask) * kQCols, 1u);
         }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < kQCols * kQBins; i += kQThreads) {
-        const int c = i / kQBins, b = i % kQBins;
+        const int c = i % kQCols, b = i / kQCols;
         const int64_t gc = static_cast<int64_t>(blockIdx.x) * kQCols + c;
-        const uint32_t n = h[c * kQPitch + b];
+        const uint32_t n = h[i];
         if (gc < K && n) atomicAdd(hist + gc * kQBins + b, n);
     }
 }
