@@ -34,38 +34,40 @@ namespace {
 constexpr int kLnThreads = 256;
 
 // Block-wide max of non-negative values; every lane receives the result.
-__device__ __forceinline__ float block_max(float v, float* red) {
+// `red` holds two slots of 16 floats used by alternate rows (parity), so one
+// barrier separates a call's writes from its reads: the next call writes the
+// other slot, and the call after it passes that call's barrier first, which
+// every wave reaches only after reading this slot.
+__device__ __forceinline__ float block_max(float v, float* red, int parity) {
     v = wave_max(v);
     const int nw = blockDim.x >> 6;
     if (nw == 1) return v;
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    float* r = red + (parity & 1) * 16;
+    if ((threadIdx.x & 63) == 0) r[threadIdx.x >> 6] = v;
     __syncthreads();
-    float m = red[0];
-    for (int i = 1; i < nw; ++i) m = fmaxf(m, red[i]);
-    __syncthreads();
+    float m = r[0];
+    for (int i = 1; i < nw; ++i) m = fmaxf(m, r[i]);
     return m;
 }
 
 // Canonical halving tree over the 256 lane partials:
-// p[i] = p[i] + p[i+d] for d = 128, 64, ..., 1.  Every lane gets p[0].
-__device__ __forceinline__ float canonical_tree(float p, float* lds) {
+// p[i] = p[i] + p[i+d] for d = 128, 64, ..., 1.  Every lane gets p[0].  After
+// one barrier each wave evaluates the whole tree itself from the partials in
+// `part` (256 floats, one region per reduction of a row: the row's other
+// barriers lie between a region's reads and its next writes): lane l forms
+// (p[l] + p[l+128]) + (p[l+64] + p[l+192]), which is p[l] after d = 64, and
+// the steps d = 32..1 run on the wave's lanes.
+__device__ __forceinline__ float canonical_tree(float p, float* part) {
     const int tid = threadIdx.x;
-    lds[tid] = p;
+    part[tid] = p;
     __syncthreads();
-    if (tid < 128) lds[tid] = lds[tid] + lds[tid + 128];
-    __syncthreads();
-    if (tid < 64) lds[tid] = lds[tid] + lds[tid + 64];
-    __syncthreads();
-    if (tid < 64) {
-        float v = lds[tid];
+    const int l = tid & 63;
+    const float a = part[l] + part[l + 128];
+    const float b = part[l + 64] + part[l + 192];
+    float v = a + b;
 #pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) v = v + __shfl_down(v, d, 64);
-        if (tid == 0) lds[256] = v;
-    }
-    __syncthreads();
-    const float r = lds[256];
-    __syncthreads();
-    return r;
+    for (int d = 32; d >= 1; d >>= 1) v = v + __shfl_down(v, d, 64);
+    return __shfl(v, 0, 64);
 }
 
 // RN(1/s) of a chunk's eight column factors (rcp_rn), with the range test taken
@@ -148,7 +150,8 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
     const float* __restrict__ static_scale, int8_t* __restrict__ xq,
     float* __restrict__ x_scale, float* __restrict__ rowmax, unsigned long long* __restrict__ clip,
     uint32_t* __restrict__ clip_ch) {
-    __shared__ float lds[kLnThreads + 4];
+    // [0, 256): mean partials, [256, 512): variance partials, [512, 544): row maxima
+    __shared__ float lds[2 * kLnThreads + 32];
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
     const int64_t chunks = K / kChunk;
@@ -195,7 +198,8 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
         rd_static = 1.0f / d_static;
     }
     int nclip = 0;
-    for (int64_t m = blockIdx.x; m < M; m += G) {
+    int parity = 0;
+    for (int64_t m = blockIdx.x; m < M; m += G, parity ^= 1) {
         if (m + D * G < M) fetch(m + D * G, ring[D]);
         float v[CPT][kChunk];
 #pragma unroll
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
                     }
                 }
             }
-            const float var = canonical_tree(p, lds) / kf;
+            const float var = canonical_tree(p, lds + kLnThreads) / kf;
             const float rho = 1.0f / __builtin_sqrtf(var + eps);
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
                     for (int e = 0; e < kChunk; ++e) mx = fmaxf(mx, fabsf(v[i][e]));
                 }
             }
-            mx = block_max(mx, lds);
+            mx = block_max(mx, lds + 2 * kLnThreads, parity);
             d = step_from_absmax(mx);
             rd = 1.0f / d;
             if (tid == 0) {
@@ -443,12 +447,14 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_stream_kernel(
     const float* __restrict__ static_scale, int8_t* __restrict__ xq,
     float* __restrict__ x_scale, float* __restrict__ rowmax, unsigned long long* __restrict__ clip,
     uint32_t* __restrict__ clip_ch) {
-    __shared__ float lds[kLnThreads + 4];
+    // [0, 256): mean partials, [256, 512): variance partials, [512, 544): row maxima
+    __shared__ float lds[2 * kLnThreads + 32];
     const int tid = threadIdx.x;
     const int64_t chunks = K / kChunk;
     const float kf = static_cast<float>(K);
     int nclip = 0;
-    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+    int parity = 0;
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x, parity ^= 1) {
         const T* row = x + m * K;
         float mu = 0.0f, rho = 0.0f;
         if (LN) {
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_stream_kernel(
                     p = p + dd;
                 }
             }
-            const float var = canonical_tree(p, lds) / kf;
+            const float var = canonical_tree(p, lds + kLnThreads) / kf;
             rho = 1.0f / __builtin_sqrtf(var + eps);
         }
         float d, rd;
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_stream_kernel(
 #pragma unroll
                 for (int e = 0; e < kChunk; ++e) mx = fmaxf(mx, fabsf(v[e]));
             }
-            mx = block_max(mx, lds);
+            mx = block_max(mx, lds + 2 * kLnThreads, parity);
             d = step_from_absmax(mx);
             if (rowmax) {
                 if (tid == 0) rowmax[m] = mx;
