@@ -17,7 +17,8 @@
 // Kernels, chosen by launch_gemm from the shape:
 //   gemm_pp_kernel      M > 64, K % 128 == 0: 256x128 or 256x256 tiles, eight
 //                       waves in two groups alternating memory and compute
-//                       phases ("ping-pong"), three LDS stages filled by
+//                       phases ("ping-pong"), LDS stages of 128 K-bytes
+//                       (three for 256x128, two for 256x256) filled by
 //                       direct-to-LDS transfers
 //   gemm_pp_mixed_kernel  both ping-pong tiles in one launch: 256x256 over the
 //                       first columns, 256x128 over the rest, when that fills
@@ -550,6 +551,13 @@ __device__ __forceinline__ void dma16(const int8_t* base, uint32_t voff, uint32_
 // LDS bytes of the operand stages of one configuration
 template <int BM, int BN, int BK, int STAGES>
 constexpr int pp_stage_lds() { return STAGES * (BM + BN) * BK; }
+// With two stages (the 256x256 tile with 128-byte K stages, 128 KB of LDS)
+// group 0 moves every stage: it issues all transfers of stage t+1 at the start
+// of its memory phase of stage t -- into the buffer of stage t-1, which group 0
+// read one phase and group 1 read in the phase just closed -- and waits for
+// them at the end of its compute phase of stage t, so stage t+1 has landed
+// before the barrier that precedes either group's memory phase of stage t+1
+// (two phases of lookahead).  Group 1 issues no transfers.
 
 // One BM x BN output tile at rows [tm * BM, ...) and columns
 // [n_base + tn * BN, ...), where (tm, tn) is tile `pid` of a tiles_m x tiles_n
@@ -567,11 +575,13 @@ __device__ __forceinline__ void pp_tile(
     constexpr int kStageBytes = kRows * BK;
     constexpr int kCPR = BK / 16;            // 16-byte chunks per row
     constexpr int kRowsPerXfer = 1024 / BK;  // 1 KB per wave-wide transfer
-    constexpr int IPW = kRows / kRowsPerXfer / 8;
+    constexpr bool TWO = STAGES == 2;                 // group 0 moves every stage
+    constexpr int kIssuers = TWO ? 4 : 8;
+    constexpr int IPW = kRows / kRowsPerXfer / kIssuers;
     constexpr int NKK = BK / 32;
-    static_assert(IPW * 8 * kRowsPerXfer == kRows, "stage divides over the waves");
+    static_assert(IPW * kIssuers * kRowsPerXfer == kRows, "stage divides over the waves");
     static_assert(BM % kRowsPerXfer == 0, "a transfer never straddles A and B");
-    static_assert(STAGES >= 3, "a refill needs two phases of slack");
+    static_assert(STAGES >= 2, "two stages at least");
     constexpr int kEpiPitch = epi_pitch<OUT, T::TN>();
     static_assert(8 * 32 * kEpiPitch <= STAGES * kStageBytes, "epilogue scratch fits");
     static_assert(BM + BN <= 512, "one scale per thread");
@@ -585,25 +595,39 @@ __device__ __forceinline__ void pp_tile(
     const int group = wave >> 2;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    int src_off[IPW];
-    bool src_a[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int x = wave * IPW + i;
+    // lane q of transfer x lands at LDS byte 16 q of the transfer's 1 KB and
+    // fetches the global chunk whose swizzled slot that is.  With three or
+    // more stages the offsets are kept in registers; with two, group 0's 16
+    // transfers per wave are addressed as they are issued (registers are short)
+    constexpr int kOff = TWO ? 1 : IPW;
+    int src_off[kOff];
+    bool src_a[kOff];
+    auto src = [&](int x, bool& is_a) {
         const int q = x * 64 + lane;
         const int row = q / kCPR;
         const int c = (q % kCPR) ^ swz_k<BK>(row);
-        src_a[i] = x * kRowsPerXfer < BM;
-        src_off[i] = src_a[i] ? min(m0 + row, M - 1) * K + c * 16
-                              : min(n0 + row - BM, N - 1) * K + c * 16;
+        is_a = x * kRowsPerXfer < BM;
+        return is_a ? min(m0 + row, M - 1) * K + c * 16 : min(n0 + row - BM, N - 1) * K + c * 16;
+    };
+    if constexpr (!TWO) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) src_off[i] = src(wave * IPW + i, src_a[i]);
     }
     const int KT = K / BK;
     auto issue = [&](int t) {
         int8_t* stage = lds + (t % STAGES) * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < IPW; ++i)
-            dma16(src_a[i] ? A : B, static_cast<uint32_t>(src_off[i] + t * BK),
-                  lds_addr(stage + (wave * IPW + i) * 1024));
+        for (int i = 0; i < IPW; ++i) {
+            const int x = wave * IPW + i;
+            if constexpr (TWO) {
+                bool a;
+                const int off = src(x, a);
+                dma16(a ? A : B, static_cast<uint32_t>(off + t * BK), lds_addr(stage + x * 1024));
+            } else {
+                dma16(src_a[i] ? A : B, static_cast<uint32_t>(src_off[i] + t * BK),
+                      lds_addr(stage + x * 1024));
+            }
+        }
     };
     // wait for this wave's transfers of stage t; later stages may stay in flight
     auto wait_stage = [&](int t) {
@@ -646,8 +670,20 @@ __device__ __forceinline__ void pp_tile(
     const float D = (OUT == kOutI8) ? *epi.next_step : 1.0f;
     const float rD = 1.0f / D;
     compiler_fence();
-    for (int t = 0; t < STAGES - 1 && t < KT; ++t) issue(t);
-    wait_stage(0);
+    if constexpr (TWO) {
+        if (group == 0) {
+            issue(0);
+            if (KT > 1) {
+                issue(1);
+                wait_vmcnt<IPW>();
+            } else {
+                wait_vmcnt<0>();
+            }
+        }
+    } else {
+        for (int t = 0; t < STAGES - 1 && t < KT; ++t) issue(t);
+        wait_stage(0);
+    }
     if (OUT != kOutI32 && st < BM + BN) scales[st] = scale;
     if (OUT != kOutI32 && st < BN) {
         epi_cols[st] = cb;
@@ -658,7 +694,11 @@ __device__ __forceinline__ void pp_tile(
     if (group == 1) bar();
     for (int t = 0; t < KT; ++t) {
         // memory phase
-        if (t + STAGES - 1 < KT) issue(t + STAGES - 1);
+        if constexpr (TWO) {
+            if (group == 0 && t >= 1 && t + 1 < KT) issue(t + 1);
+        } else {
+            if (t + STAGES - 1 < KT) issue(t + STAGES - 1);
+        }
         const int8_t* S = lds + (t % STAGES) * kStageBytes;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
@@ -673,7 +713,7 @@ __device__ __forceinline__ void pp_tile(
         }
         compiler_fence();
         wait_lgkmcnt0();
-        if (group == 1 && t + 1 < KT) wait_stage(t + 1);
+        if (!TWO && group == 1 && t + 1 < KT) wait_stage(t + 1);
         bar();
         // compute phase
 #pragma unroll
@@ -685,7 +725,10 @@ __device__ __forceinline__ void pp_tile(
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[kk][j], fa[kk][i],
                                                                       acc[i][j], 0, 0, 0);
         compiler_fence();
-        if (group == 0 && t + 1 < KT) wait_stage(t + 1);
+        if (group == 0 && t + 1 < KT) {
+            if constexpr (TWO) wait_vmcnt<0>();
+            else wait_stage(t + 1);
+        }
         bar();
     }
     if (group == 0) bar();
@@ -731,8 +774,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_mixed_kernel(
     int sx_per_token, const float* __restrict__ sw, int sw_per_tensor, void* __restrict__ Y,
     int M, int N, int K, Epi epi, Batch bat, int nb_big) {
     SQ_APPLY_BATCH(OUT);
-    constexpr int kLds = pp_stage_lds<256, 256, 64, 3>() > pp_stage_lds<256, 128, 128, 3>()
-                             ? pp_stage_lds<256, 256, 64, 3>()
+    constexpr int kLds = pp_stage_lds<256, 256, 128, 2>() > pp_stage_lds<256, 128, 128, 3>()
+                             ? pp_stage_lds<256, 256, 128, 2>()
                              : pp_stage_lds<256, 128, 128, 3>();
     __shared__ __attribute__((aligned(1024))) int8_t lds[kLds];
     __shared__ __attribute__((aligned(16))) float scales[512];
@@ -741,7 +784,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_mixed_kernel(
     const int big = tiles_m * nb_big;
     const int pid = blockIdx.x;
     if (pid < big) {
-        pp_tile<256, 256, 2, 4, 64, 3, OUT>(A, B, sx, sx_per_token, sw, sw_per_tensor, Y, M, N, K,
+        pp_tile<256, 256, 2, 4, 128, 2, OUT>(A, B, sx, sx_per_token, sw, sw_per_tensor, Y, M, N, K,
                                             epi, pid, tiles_m, nb_big, 0, lds, scales, epi_cols);
     } else {
         const int n_base = 256 * nb_big;
@@ -1183,7 +1226,7 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool x_per_token,
             }
         }
         if (best_nb == nb_all)
-            return run_pp<256, 256, 2, 4, 64, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
+            return run_pp<256, 256, 2, 4, 128, 2>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
                                                  out_kind, epi, bat, stream);
         if (best_nb == 0)
             return run_pp<256, 128, 4, 2, 128, 3>(xq, x_scale, x_per_token, wq, w_scale, w_per_tensor, m, n, k, y,
