@@ -2,7 +2,7 @@
 [Review] §5.6, Fig. 6: the batched matrix multiplications of attention run in
 INT8 like the linear layers) against the oracle, bit for bit: small batches
 reaching every GEMM kernel (short K for head dimensions 64, 128 and 256,
-ping-pong, skinny, register-staged), every step granularity and shared (stride 0) operands; and the
+ping-pong, both ping-pong tiles in one launch, skinny, register-staged), every step granularity and shared (stride 0) operands; and the
 OPT-6.7B-shaped attention (32 heads, 2048 tokens, head dimension 128): scores
 S = Q K^T and output O = P V with operands quantized per token by
 sq_smooth_quantize_act (s = 1), checked on sampled heads.
@@ -45,6 +45,9 @@ CASES = [
     (2, 150, 90, 192, "per_token", "per_channel", False),    # register-staged (K % 128 != 0)
     (2, 1, 2048, 128, "per_token", "per_channel", False),    # one query token (decode)
     (2, 96, 128, 512, "dynamic_per_tensor", "per_tensor", False),
+    # two tile sizes in one launch (256x256 over the first 16384 columns of both entries,
+    # 256x128 over the rest): the tile choice counts the batch entries
+    (2, 257, 20000, 384, "per_token", "per_channel", False),
 ]
 
 
