@@ -205,59 +205,103 @@ hipError_t run_quantile(const T* x, int64_t rows, int64_t K, int64_t rank0, floa
 
 // ---- alpha search -----------------------------------------------------------
 
-__device__ __forceinline__ double to_f64(uint16_t b) {
-    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(b) << 16));
-}
-__device__ __forceinline__ double to_f64(float v) { return static_cast<double>(v); }
-
 // Y[m, n] = sum_k X[m, k] W[n, k] in fp64 (the inputs' products are exact in
-// fp64).  64 x 64 output tile per block, 4 x 4 outputs per thread (rows ty +
-// 16 i, columns tx + 16 j), K in steps of 16 staged in LDS.
-constexpr int kRT = 64;
+// fp64).  128 x 128 output tile per block, 8 x 8 outputs per thread (rows ty +
+// 16 i, columns tx + 16 j), K in steps of 16 staged in LDS: each step's rows
+// arrive as 16-byte loads (8 bf16 or 4 fp32 per lane), all issued before any
+// is converted.  Each output accumulates in increasing k, one fma per k.
+constexpr int kRT = 128;
 constexpr int kRK = 16;
+
+// Elements of a 16-byte chunk of T, as doubles.
+__device__ __forceinline__ void chunk_f64(const uint4& v, double (&d)[8], uint16_t) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        d[2 * e] = static_cast<double>(__uint_as_float(u[e] << 16));
+        d[2 * e + 1] = static_cast<double>(__uint_as_float(u[e] & 0xffff0000u));
+    }
+}
+__device__ __forceinline__ void chunk_f64(const uint4& v, double (&d)[8], float) {
+    d[0] = static_cast<double>(__uint_as_float(v.x));
+    d[1] = static_cast<double>(__uint_as_float(v.y));
+    d[2] = static_cast<double>(__uint_as_float(v.z));
+    d[3] = static_cast<double>(__uint_as_float(v.w));
+}
+
+// One operand's rows [r0, r0 + kRT) x columns [k0, k0 + kRK) of a row-major
+// [rows, K] tensor: the 16-byte chunks this thread loads (zero past `rows`).
+template <typename T>
+struct RefStage {
+    static constexpr int E = 16 / sizeof(T);        // elements per chunk
+    static constexpr int CPR = kRK / E;             // chunks per row
+    static constexpr int LOADS = kRT * CPR / 256;   // chunks per thread
+    static_assert(LOADS * 256 == kRT * CPR, "whole chunks per thread");
+    uint4 v[LOADS];
+    __device__ void load(const T* __restrict__ p, int64_t r0, int64_t rows, int64_t K, int64_t k0) {
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l) {
+            const int q = threadIdx.x + 256 * l;
+            const int64_t r = r0 + q / CPR;
+            v[l] = r < rows ? *reinterpret_cast<const uint4*>(p + r * K + k0 + (q % CPR) * E)
+                            : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ void store(double (*S)[kRT + 1]) const {
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l) {
+            const int q = threadIdx.x + 256 * l;
+            const int r = q / CPR, c = q % CPR;
+            double d[8];
+            chunk_f64(v[l], d, T{});
+#pragma unroll
+            for (int e = 0; e < E; ++e) S[c * E + e][r] = d[e];
+        }
+    }
+};
 
 template <typename TX, typename TW>
 __global__ __launch_bounds__(256) void ref_gemm_f64_kernel(const TX* __restrict__ x,
                                                            const TW* __restrict__ w, int64_t M,
                                                            int64_t N, int64_t K,
                                                            double* __restrict__ y) {
+    constexpr int R = kRT / 16;
     __shared__ double As[kRK][kRT + 1];
     __shared__ double Bs[kRK][kRT + 1];
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
     const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRT;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRT;
-    double acc[4][4];
+    double acc[R][R];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+        for (int j = 0; j < R; ++j) acc[i][j] = 0.0;
+    RefStage<TX> sa;
+    RefStage<TW> sb;
     for (int64_t k0 = 0; k0 < K; k0 += kRK) {
-        for (int i = threadIdx.x; i < kRT * kRK; i += 256) {
-            const int r = i / kRK, kk = i % kRK;
-            const int64_t k = k0 + kk;
-            const int64_t m = m0 + r, n = n0 + r;
-            As[kk][r] = (m < M && k < K) ? to_f64(x[m * K + k]) : 0.0;
-            Bs[kk][r] = (n < N && k < K) ? to_f64(w[n * K + k]) : 0.0;
-        }
+        sa.load(x, m0, M, K, k0);
+        sb.load(w, n0, N, K, k0);
+        sa.store(As);
+        sb.store(Bs);
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < kRK; ++kk) {
-            double a[4], b[4];
+            double a[R], b[R];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+            for (int i = 0; i < R; ++i) a[i] = As[kk][ty + 16 * i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+            for (int j = 0; j < R; ++j) b[j] = Bs[kk][tx + 16 * j];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < R; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < R; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < R; ++j) {
             const int64_t m = m0 + ty + 16 * i, n = n0 + tx + 16 * j;
             if (m < M && n < N) y[m * N + n] = acc[i][j];
         }
