@@ -218,9 +218,9 @@ constexpr int kFactorThreads = 64 * kFactorWaves;
 // [0, splits_x)) and W (rows [splits_x, splits_x + splits_w)) into a_j and w_j
 // (floored) and store them; otherwise a_j and w_j are already in a and w.  The
 // pass is latency-bound: wave g of a block takes partial rows g, g + 4, ...
-// of the block's 64 columns (eight loads in flight per batch), the four
-// results meet in LDS, and wave 0 finishes the columns (eq. (4), fold, static
-// scale).
+// of both matrices in the block's 64 columns (eight loads in flight per
+// batch, so up to 32 partial rows cost one round trip), the four results meet
+// in LDS, and wave 0 finishes the columns (eq. (4), fold, static scale).
 __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
     float* __restrict__ a, float* __restrict__ w, int64_t K, float alpha,
     const uint32_t* __restrict__ partial, int splits_x, int splits_w,
@@ -237,22 +237,26 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
          j0 += static_cast<int64_t>(gridDim.x) * kFactorCols) {
         const int64_t j = j0 + lane;
         if (partial) {
-            auto reduce = [&](int first, int count) {
-                uint32_t m = kFloorBits;
-                for (int i = g; i < count; i += 8 * kFactorWaves) {
+            // rows [0, splits_x) hold X_cal's maxima, the rest W's
+            const int total = splits_x + splits_w;
+            uint32_t mx = kFloorBits, mw = kFloorBits;
+            if (j < K) {
+                for (int i = g; i < total; i += 8 * kFactorWaves) {
                     uint32_t v[8];
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
                         const int r = i + u * kFactorWaves;
-                        v[u] = (r < count) ? partial[static_cast<int64_t>(first + r) * K + j] : 0u;
+                        v[u] = (r < total) ? partial[static_cast<int64_t>(r) * K + j] : 0u;
                     }
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) m = max(m, v[u]);
+                    for (int u = 0; u < 8; ++u) {
+                        if (i + u * kFactorWaves < splits_x) mx = max(mx, v[u]);
+                        else mw = max(mw, v[u]);
+                    }
                 }
-                return m;
-            };
-            pm[0][g][lane] = j < K ? reduce(0, splits_x) : kFloorBits;
-            pm[1][g][lane] = j < K ? reduce(splits_x, splits_w) : kFloorBits;
+            }
+            pm[0][g][lane] = mx;
+            pm[1][g][lane] = mw;
         }
         __syncthreads();
         if (g == 0 && j < K) {
