@@ -126,7 +126,11 @@ typedef enum { SQ_W_PER_CHANNEL = 0, SQ_W_PER_TENSOR = 1 } sq_weight_mode;
  *   x_absmax, w_absmax [K] fp32: a_j and w_j (required; they also serve as the
  *                 library's working memory for the two column maxima)
  * Kernels: the column-absmax pass over X_cal and W, the factor pass, one
- * weight smooth+quantize pass; reads X_cal once and W twice.  SQ_W_PER_TENSOR
+ * weight smooth+quantize pass; reads X_cal once and W twice.  The column-absmax
+ * pass stages its per-block maxima in wq (written last, by the quantize pass)
+ * when wq has room for them, else it folds them with atomics into x_absmax and
+ * w_absmax; wq's contents are defined only once the call has completed on the
+ * stream.  SQ_W_PER_TENSOR
  * adds a smoothed-row-maximum pass over W (staged in wq) and a one-block
  * reduction before the quantize pass, which then uses the single step.
  */
