@@ -130,9 +130,11 @@ typedef enum { SQ_W_PER_CHANNEL = 0, SQ_W_PER_TENSOR = 1 } sq_weight_mode;
  * pass stages its per-block maxima in wq (written last, by the quantize pass)
  * when wq has room for them, else it folds them with atomics into x_absmax and
  * w_absmax; wq's contents are defined only once the call has completed on the
- * stream.  SQ_W_PER_TENSOR
- * adds a smoothed-row-maximum pass over W (staged in wq) and a one-block
- * reduction before the quantize pass, which then uses the single step.
+ * stream.  SQ_W_PER_TENSOR: the largest smoothed weight magnitude is
+ * max_j RN(max_n |W[n,j]| * s_j) (rounding and multiplying by s_j > 0 are
+ * monotone), taken from the column maxima in the factor pass and held in
+ * w_scale[0] until a one-thread kernel replaces it with the step; W is still
+ * read twice, and the quantize pass uses the single step.
  */
 sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T,
                        const void* w, sq_dtype w_dt, int64_t N, int64_t K, float alpha,

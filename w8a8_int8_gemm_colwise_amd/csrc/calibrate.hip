@@ -21,6 +21,10 @@
 //   uint atomicMax per column per block)
 //   weight_quant    per output row: What = W*s, row |max|, dw_n, codes; the row
 //                   stays in registers between the max and the quantize passes
+//   per-tensor weight step: max over n, k of |RN(W[n,k]*s_k)| equals
+//                   max_k RN(max_n |W[n,k]| * s_k) (RN is monotone and s > 0), so
+//                   the factor pass takes it from the raw column maxima and the
+//                   codes need one pass over W, as per channel
 #include <algorithm>
 
 #include "sq_device.hpp"
@@ -32,14 +36,18 @@ namespace {
 constexpr uint32_t kFloorBits = 0x33d6bf95u;  // bit pattern of 1e-7f
 static_assert(sizeof(float) == 4, "fp32");
 
+// X_cal's maxima start at the floor; W's start at 0 (the raw maxima, floored by
+// the factor pass, which also needs them unfloored for the per-tensor step).
 __global__ void fill_maxima_kernel(uint32_t* __restrict__ xa, uint32_t* __restrict__ wa,
-                                   int64_t K, uint32_t* __restrict__ static_bits) {
+                                   int64_t K, uint32_t* __restrict__ static_bits,
+                                   uint32_t* __restrict__ w_tensor_bits) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < K) {
         xa[i] = kFloorBits;
-        wa[i] = kFloorBits;
+        wa[i] = 0u;
     }
     if (i == 0 && static_bits) *static_bits = 0u;
+    if (i == 0 && w_tensor_bits) *w_tensor_bits = 0u;
 }
 
 // ---- column absmax ----------------------------------------------------------
@@ -169,9 +177,11 @@ template <typename TX, typename TW>
 __global__ __launch_bounds__(kColmaxThreads) void colmax_partial_kernel(
     const TX* __restrict__ x, int64_t T, const TW* __restrict__ w, int64_t N, int64_t K,
     int segs_x, int64_t rpb_x, int segs_w, int64_t rpb_w, int splits_x,
-    uint32_t* __restrict__ partial, uint32_t* __restrict__ static_bits) {
+    uint32_t* __restrict__ partial, uint32_t* __restrict__ static_bits,
+    uint32_t* __restrict__ w_tensor_bits) {
     __shared__ uint32_t red[kColmaxWaves][64 * ColmaxLane<uint16_t>::kCols];
     if (blockIdx.x == 0 && threadIdx.x == 0 && static_bits) *static_bits = 0u;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && w_tensor_bits) *w_tensor_bits = 0u;
     int64_t b = blockIdx.x;
     const int64_t nbx = static_cast<int64_t>(segs_x) * splits_x;
     if (b < nbx) {
@@ -230,20 +240,21 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
     const uint32_t* __restrict__ partial, int splits_x, int splits_w,
     const float* __restrict__ gamma, const float* __restrict__ beta, float* __restrict__ s,
     float* __restrict__ gamma_s, float* __restrict__ beta_s, uint32_t* __restrict__ static_bits,
-    const float* __restrict__ act_stat) {
+    const float* __restrict__ act_stat, uint32_t* __restrict__ w_tensor_bits) {
     __shared__ uint32_t pm[2][kFactorWaves][kFactorCols];
     const int lane = threadIdx.x & 63;
     const int g = threadIdx.x >> 6;
     const double al = static_cast<double>(alpha);
     const double be = 1.0 - al;
     float local = 0.0f;
+    float local_w = 0.0f;  // max of RN(raw w_j * s_j) over the block's columns
     for (int64_t j0 = static_cast<int64_t>(blockIdx.x) * kFactorCols; j0 < K;
          j0 += static_cast<int64_t>(gridDim.x) * kFactorCols) {
         const int64_t j = j0 + lane;
         if (partial) {
             // rows [0, splits_x) hold X_cal's maxima, the rest W's
             const int total = splits_x + splits_w;
-            uint32_t mx = kFloorBits, mw = kFloorBits;
+            uint32_t mx = kFloorBits, mw = 0u;  // W's maximum raw here, floored below
             if (j < K) {
                 for (int i = g; i < total; i += 8 * kFactorWaves) {
                     uint32_t v[8];
@@ -264,7 +275,7 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
         }
         __syncthreads();
         if (g == 0 && j < K) {
-            float aj, wj;
+            float aj, wraw;
             if (partial) {
                 uint32_t ab = pm[0][0][lane], wb = pm[1][0][lane];
 #pragma unroll
@@ -273,13 +284,14 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
                     wb = max(wb, pm[1][q][lane]);
                 }
                 aj = __uint_as_float(ab);
-                wj = __uint_as_float(wb);
+                wraw = __uint_as_float(wb);
                 a[j] = aj;
-                w[j] = wj;
             } else {
                 aj = a[j];
-                wj = w[j];
+                wraw = w[j];
             }
+            const float wj = fmaxf(wraw, kFloor);
+            w[j] = wj;
             if (act_stat) {
                 // a given per-channel activation statistic replaces the peak
                 aj = fmaxf(act_stat[j], kFloor);
@@ -296,12 +308,30 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
             // RN(max(FLOOR, x)/127) is monotone in x, so the max of the per-channel
             // steps is the step of the max smoothed calibration peak RN(a_j/s_j).
             local = fmaxf(local, step_from_absmax(aj / sj));
+            // the largest smoothed weight magnitude in column j is RN(raw w_j * s_j)
+            local_w = fmaxf(local_w, wraw * sj);
         }
         __syncthreads();  // pm is refilled by the next columns
     }
-    if (!static_bits || g != 0) return;
-    local = wave_max(local);
-    if (lane == 0) atomicMax(static_bits, __float_as_uint(local));
+    if (g != 0) return;
+    // non-negative floats order like their bit patterns
+    if (static_bits) {
+        local = wave_max(local);
+        if (lane == 0) atomicMax(static_bits, __float_as_uint(local));
+    }
+    if (w_tensor_bits) {
+        local_w = wave_max(local_w);
+        if (lane == 0) atomicMax(w_tensor_bits, __float_as_uint(local_w));
+    }
+}
+
+// The per-tensor weight step from the maximum smoothed weight magnitude held
+// as bits in the same word: RN(max(FLOOR, m) / 127).
+__global__ void weight_tensor_step_kernel(uint32_t* word) {
+    if (threadIdx.x == 0) {
+        const float m = __uint_as_float(word[0]);
+        reinterpret_cast<float*>(word)[0] = step_from_absmax(m);
+    }
 }
 
 // ---- weight smoothing + per-output-channel quantization ------------------------
@@ -312,11 +342,10 @@ __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
 // row the block walks, and the loads of the block's next D rows are in flight
 // while the current row is reduced and quantized (a ring of D+1 rows).  The
 // row stays in registers between the absmax and the quantize passes.
-// What the weight kernels produce per row n (the third argument `ws`):
-//   kWChannel  step dw_n = RN(max(FLOOR, max_k |What|) / 127) into ws[n], codes
-//   kWRowMax   the raw maximum max_k |What| into ws[n] (float scratch), no codes
-//   kWGiven    codes with the step read from ws[0] (per-tensor), ws not written
-enum WMode : int { kWChannel = 0, kWRowMax = 1, kWGiven = 2 };
+// What the weight kernels produce per row n (the argument `w_scale`):
+//   kWChannel  step dw_n = RN(max(FLOOR, max_k |What|) / 127) into w_scale[n], codes
+//   kWGiven    codes with the step read from w_scale[0] (per tensor), not written
+enum WMode : int { kWChannel = 0, kWGiven = 2 };
 
 template <typename T, int CPT, int D, int MAXT = 1024, int WM = kWChannel>
 __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
@@ -387,19 +416,17 @@ __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
             }
             d = step_from_absmax(m);
             rd = 1.0f / d;
-            if (tid == 0) w_scale[n] = (WM == kWRowMax) ? m : d;
+            if (tid == 0) w_scale[n] = d;
         }
-        if (WM != kWRowMax) {
-            int8_t* orow = wq + n * K;
+        int8_t* orow = wq + n * K;
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const int64_t c = tid + static_cast<int64_t>(i) * nthr;
-                if (c < chunks) {
-                    int q[kChunk];
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
+            if (c < chunks) {
+                int q[kChunk];
 #pragma unroll
-                    for (int e = 0; e < kChunk; ++e) q[e] = code_of(div_rn(v[i][e], d, rd));
-                    *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
-                }
+                for (int e = 0; e < kChunk; ++e) q[e] = code_of(div_rn(v[i][e], d, rd));
+                *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
             }
         }
 #pragma unroll
@@ -436,8 +463,7 @@ __global__ __launch_bounds__(256) void weight_quant_stream_kernel(
             m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
             __syncthreads();
             d = step_from_absmax(m);
-            if (tid == 0) w_scale[n] = (WM == kWRowMax) ? m : d;
-            if (WM == kWRowMax) continue;
+            if (tid == 0) w_scale[n] = d;
         }
         const float rd = 1.0f / d;
         for (int64_t c = tid; c < chunks; c += 256) {
@@ -485,18 +511,12 @@ hipError_t launch_weight_quant_mode(const T* w, int64_t N, int64_t K, const floa
     return hipGetLastError();
 }
 
-// Per output channel: one pass.  Per tensor: the smoothed row maxima (staged
-// as floats in wq, which only the last pass writes), the one-block reduction
-// into w_scale[0], then the codes with that single step.
+// One pass over W: per output channel the kernel finds each row's step; per
+// tensor the step is already in w_scale[0] (from the factor pass).
 template <typename T>
 hipError_t launch_weight_quant(const T* w, int64_t N, int64_t K, const float* s, int8_t* wq,
                                float* w_scale, bool per_tensor, hipStream_t stream) {
     if (!per_tensor) return launch_weight_quant_mode<T, kWChannel>(w, N, K, s, wq, w_scale, stream);
-    float* rowmax = reinterpret_cast<float*>(wq);  // 4N bytes <= N*K bytes (K >= 64)
-    hipError_t e = launch_weight_quant_mode<T, kWRowMax>(w, N, K, s, wq, rowmax, stream);
-    if (e != hipSuccess) return e;
-    e = launch_tensor_step(rowmax, N, w_scale, stream);
-    if (e != hipSuccess) return e;
     return launch_weight_quant_mode<T, kWGiven>(w, N, K, s, wq, w_scale, stream);
 }
 
@@ -560,11 +580,12 @@ void plan_joint(int64_t T, int64_t N, int64_t K, int seg_x, int seg_w, Split& px
 template <typename TX, typename TW>
 hipError_t launch_partial(const TX* x, int64_t T, const TW* w, int64_t N, int64_t K,
                           const Split& px, const Split& pw, uint32_t* partial,
-                          uint32_t* static_bits, hipStream_t stream) {
+                          uint32_t* static_bits, uint32_t* w_tensor_bits, hipStream_t stream) {
     const int64_t blocks = static_cast<int64_t>(px.segs) * px.splits +
                            static_cast<int64_t>(pw.segs) * pw.splits;
     colmax_partial_kernel<TX, TW><<<static_cast<unsigned>(blocks), kColmaxThreads, 0, stream>>>(
-        x, T, w, N, K, px.segs, px.rpb, pw.segs, pw.rpb, px.splits, partial, static_bits);
+        x, T, w, N, K, px.segs, px.rpb, pw.segs, pw.rpb, px.splits, partial, static_bits,
+        w_tensor_bits);
     return hipGetLastError();
 }
 
@@ -585,6 +606,9 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
     uint32_t* xa = reinterpret_cast<uint32_t*>(x_absmax);
     uint32_t* wa = reinterpret_cast<uint32_t*>(w_absmax);
     uint32_t* sb = reinterpret_cast<uint32_t*>(act_scale_static);
+    // per tensor: w_scale[0] first holds the bits of the largest smoothed weight
+    // magnitude (zeroed by the first kernel, raised by the factor pass), then the step
+    uint32_t* wt = w_per_tensor ? reinterpret_cast<uint32_t*>(w_scale) : nullptr;
     hipError_t e;
 
     // The per-block column maxima need (splits_x + splits_w) * K words of
@@ -597,16 +621,16 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
     uint32_t* partial = use_partial ? reinterpret_cast<uint32_t*>(wq) : nullptr;
     if (use_partial) {
         if (x_dt == Dt::BF16 && w_dt == Dt::BF16)
-            e = launch_partial(static_cast<const uint16_t*>(x_cal), T, static_cast<const uint16_t*>(w), N, K, px, pw, partial, sb, stream);
+            e = launch_partial(static_cast<const uint16_t*>(x_cal), T, static_cast<const uint16_t*>(w), N, K, px, pw, partial, sb, wt, stream);
         else if (x_dt == Dt::BF16)
-            e = launch_partial(static_cast<const uint16_t*>(x_cal), T, static_cast<const float*>(w), N, K, px, pw, partial, sb, stream);
+            e = launch_partial(static_cast<const uint16_t*>(x_cal), T, static_cast<const float*>(w), N, K, px, pw, partial, sb, wt, stream);
         else if (w_dt == Dt::BF16)
-            e = launch_partial(static_cast<const float*>(x_cal), T, static_cast<const uint16_t*>(w), N, K, px, pw, partial, sb, stream);
+            e = launch_partial(static_cast<const float*>(x_cal), T, static_cast<const uint16_t*>(w), N, K, px, pw, partial, sb, wt, stream);
         else
-            e = launch_partial(static_cast<const float*>(x_cal), T, static_cast<const float*>(w), N, K, px, pw, partial, sb, stream);
+            e = launch_partial(static_cast<const float*>(x_cal), T, static_cast<const float*>(w), N, K, px, pw, partial, sb, wt, stream);
         if (e != hipSuccess) return e;
     } else {
-        fill_maxima_kernel<<<static_cast<unsigned>((K + 255) / 256), 256, 0, stream>>>(xa, wa, K, sb);
+        fill_maxima_kernel<<<static_cast<unsigned>((K + 255) / 256), 256, 0, stream>>>(xa, wa, K, sb, wt);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = (x_dt == Dt::BF16)
@@ -621,14 +645,17 @@ hipError_t launch_calibrate(const void* x_cal, Dt x_dt, int64_t T, const void* w
     const int64_t fgrid = std::min<int64_t>((K + kFactorCols - 1) / kFactorCols, 1024);
     smooth_factor_kernel<<<static_cast<unsigned>(fgrid), kFactorThreads, 0, stream>>>(
         x_absmax, w_absmax, K, alpha, partial, px.splits, pw.splits, gamma, beta, s, gamma_s,
-        beta_s, sb, act_stat);
+        beta_s, sb, act_stat, wt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-
-    if (N == 0) {
-        // no rows: the per-tensor step of an empty weight is FLOOR / 127
-        return w_per_tensor ? launch_tensor_step(nullptr, 0, w_scale, stream) : hipSuccess;
+    if (w_per_tensor) {
+        // with no rows the maximum is 0 and the step FLOOR / 127
+        weight_tensor_step_kernel<<<1, 64, 0, stream>>>(wt);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+
+    if (N == 0) return hipSuccess;
     return (w_dt == Dt::BF16)
                ? launch_weight_quant(static_cast<const uint16_t*>(w), N, K, s, wq, w_scale,
                                      w_per_tensor, stream)
