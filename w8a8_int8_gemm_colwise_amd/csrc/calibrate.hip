@@ -229,12 +229,14 @@ constexpr int kFactorWaves = 4;   // waves that split a column's per-block maxim
 constexpr int kFactorThreads = 64 * kFactorWaves;
 
 // With `partial` set, first reduce the per-block column maxima of X_cal (rows
-// [0, splits_x)) and W (rows [splits_x, splits_x + splits_w)) into a_j and w_j
-// (floored) and store them; otherwise a_j and w_j are already in a and w.  The
+// [0, splits_x)) and W (rows [splits_x, splits_x + splits_w)) into a_j
+// (floored) and W's raw column maximum; otherwise a holds a_j and w the raw
+// maxima (atomic pass).  w_j = max(FLOOR, raw) is stored in w either way.  The
 // pass is latency-bound: wave g of a block takes partial rows g, g + 4, ...
 // of both matrices in the block's 64 columns (eight loads in flight per
 // batch, so up to 32 partial rows cost one round trip), the four results meet
-// in LDS, and wave 0 finishes the columns (eq. (4), fold, static scale).
+// in LDS, and wave 0 finishes the columns (eq. (4), fold, static scale, and
+// with w_tensor_bits the largest smoothed weight RN(raw * s_j)).
 __global__ __launch_bounds__(kFactorThreads) void smooth_factor_kernel(
     float* __restrict__ a, float* __restrict__ w, int64_t K, float alpha,
     const uint32_t* __restrict__ partial, int splits_x, int splits_w,
