@@ -443,6 +443,27 @@ def test_per_tensor_hand_example():
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
+def test_per_tensor_weight_step_from_column_maxima(seed):
+    """Invariant of the per-tensor weight step ([Review] §6.3): rounding and a
+    multiplication by s_k > 0 are monotone, so max over n, k of |RN(W[n,k] s_k)|
+    equals max_k RN(max_n |W[n,k]| s_k); the step is RN(max(FLOOR, that) / 127).
+    Checked on bf16 weights with outlier and all-zero columns and s spread over
+    six decades, the step computed from the column maxima in numpy fp32."""
+    rng = np.random.default_rng(500 + seed)
+    N, K = 96, 320
+    w = rng.standard_normal((N, K)).astype(np.float32) * 0.02
+    w[:, rng.choice(K, 4, replace=False)] *= 300.0
+    w[:, rng.choice(K, 3, replace=False)] = 0.0
+    w = datagen.bf16_bits_to_f32(datagen.f32_to_bf16_bits(w))
+    s = (10.0 ** rng.uniform(-3, 3, K)).astype(np.float32)
+    _, dw = oracle.weight_quant_per_tensor(w, s)
+    colmax = np.abs(w).max(axis=0).astype(np.float32)
+    m = np.max(colmax * s)  # fp32 products, each rounded once
+    step = np.float32(max(np.float32(1e-7), m)) / np.float32(127.0)
+    assert _bits(dw[0]) == _bits(step)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
 def test_per_tensor_step_is_max_of_finer_steps(seed):
     """step = RN(max(FLOOR, m)/127) is monotone in m, so the per-tensor weight
     step equals the largest per-output-channel step and the dynamic per-tensor
