@@ -463,6 +463,124 @@ def bench_robust(args, attain_fn):
     return out
 
 
+def smoothed_spread(absmax, s, weight: bool = False) -> float:
+    """Spread max_j / min_j of the smoothed channel peaks: RN(a_j / s_j) for the
+    activation (weight: RN(w_j * s_j)), one fp32 operation per channel as in the
+    kernels ([Review] §5.3 eq. (4): alpha = 1 gives a_j / s_j = 1 exactly)."""
+    a = np.asarray(absmax, np.float32)
+    s = np.asarray(s, np.float32)
+    m = (a * s) if weight else (a / s)
+    return float(np.float64(m.max()) / np.float64(m.min()))
+
+
+def ln_linear_f64(x_f32, gamma, beta, w_f32, eps: float = 1e-5):
+    """Y64 = LN(x) W^T in fp64: mean and biased variance per token, then
+    (x - mu) / sqrt(var + eps) * gamma + beta ([Edge] §二), times W [N, K]."""
+    x = np.asarray(x_f32, np.float64)
+    mu = x.mean(axis=1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+    h = (x - mu) / np.sqrt(var + eps) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+    return h @ np.asarray(w_f32, np.float64).T
+
+
+def alpha_sweep(args, L, dev, alphas=(0.0, 0.25, 0.5, 0.75, 0.85, 1.0), sample_every: int = 64):
+    """The LayerNorm workload's alpha sweep ([Review] §5.3 eq. (4) and §7.7:
+    migration strength; [Edge] §二: the LayerNorm with gamma/s, beta/s folded
+    in).  For every alpha and both static per-tensor and per-token steps:
+    sq_calibrate on the 65536 calibration tokens, then the fused LayerNorm +
+    int8 quantizer on the 4096 evaluation tokens and the W8A8 GEMM (4096 x
+    22016 x 8192), each timed with HIP events over ``args.steps`` calls; the
+    spread of the smoothed activation (and weight) channel peaks; the saturated
+    codes of the static step (sq_clip_count); and the relative Frobenius error
+    of the int8 path's fp32 output against LN(x) W^T in fp64, on every
+    ``sample_every``-th token (outside the timed region)."""
+    import torch
+
+    import datagen
+    import w8a8_int8_gemm_colwise_amd as sq
+
+    spec = L["spec"]
+    M, K, N = L["M"], spec.K, spec.N
+    rows = np.arange(0, M, sample_every)
+    # the fp64 reference does not depend on alpha: LN(x) W^T once
+    x_s = datagen.bf16_bits_to_f32(datagen.eval_x(spec)[rows])
+    gamma, beta = datagen.ln_params(spec)
+    w_f32 = datagen.bf16_bits_to_f32(datagen.weights(spec))
+    t0 = time.perf_counter()
+    y64 = ln_linear_f64(x_s, gamma, beta, w_f32)
+    t_ref = time.perf_counter() - t0
+    del w_f32
+    ny = float(np.linalg.norm(y64))
+    stream = torch.cuda.current_stream(dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    xs = torch.empty(M, **f32)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    y32 = torch.empty((len(rows), N), **f32)
+    rows_t = torch.from_numpy(rows).to(dev)
+    reps = max(1, args.steps)
+    out = []
+    ln_bytes = M * K * 2 + M * K + 4 * M + 8 * K
+    gemm_ops = 2.0 * M * N * K
+    for alpha in alphas:
+        cal = sq.sq_calibrate(L["xc"], L["w"], alpha, L["g"], L["b"])
+        torch.cuda.synchronize()
+        a_h, s_h = cal["x_absmax"].cpu().numpy(), cal["s"].cpu().numpy()
+        w_h = cal["w_absmax"].cpu().numpy()
+        for mode in ("static", "per_token"):
+            st = cal["static_scale"] if mode == "static" else None
+            xsa = None if mode == "static" else xs
+
+            def quant():
+                return sq.sq_smooth_quantize_act(L["x"], None, cal["ln_gamma_s"],
+                                                 cal["ln_beta_s"], 1e-5, mode, st, xq=xq,
+                                                 x_scale=xsa)
+
+            _, step = quant()
+            sq.sq_gemm_w8a8(xq, step, cal["wq"], cal["w_scale"], mode, "bf16", y=y)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+            for _ in range(reps):
+                quant()
+            ev[1].record(stream)
+            for _ in range(reps):
+                sq.sq_gemm_w8a8(xq, step, cal["wq"], cal["w_scale"], mode, "bf16", y=y)
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            t_q = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+            t_g = ev[1].elapsed_time(ev[2]) * 1e-3 / reps
+            # fp32 output of the sampled tokens for the error (untimed)
+            xq_s = xq.index_select(0, rows_t).contiguous()
+            st_s = step if mode == "static" else step.index_select(0, rows_t).contiguous()
+            sq.sq_gemm_w8a8(xq_s, st_s, cal["wq"], cal["w_scale"], mode, "f32", y=y32)
+            sat = None
+            if mode == "static":
+                cnt, _ = sq.sq_clip_count(L["x"], cal["static_scale"],
+                                          ln_gamma_s=cal["ln_gamma_s"],
+                                          ln_beta_s=cal["ln_beta_s"])
+                sat = int(cnt.item())
+            yq = y32.cpu().numpy().astype(np.float64)
+            out.append({
+                "alpha": alpha, "mode": mode,
+                "act_spread": round(smoothed_spread(a_h, s_h), 4),
+                "weight_spread": round(smoothed_spread(w_h, s_h, weight=True), 4),
+                "err_rel_fro": float(f"{np.linalg.norm(yq - y64) / ny:.4e}"),
+                "saturated_codes": sat,
+                "ln_quant_us": round(t_q * 1e6, 2),
+                "ln_quant_GBs": round(ln_bytes / t_q / 1e9, 1),
+                "gemm_us": round(t_g * 1e6, 2),
+                "gemm_TOPS": round(gemm_ops / t_g / 1e12, 1),
+            })
+    return {"alphas": list(alphas),
+            "error_sample": (f"every {sample_every}th of {M} evaluation tokens "
+                             f"({len(rows)} tokens x {N} outputs); reference LN(x) W^T in fp64 "
+                             f"({t_ref:.1f} s on the host), int8 path with fp32 output"),
+            "spread": "max_j / min_j of RN(a_j / s_j) (act) and RN(w_j * s_j) (weight) over "
+                      "the calibration peaks",
+            "rows": out}
+
+
 def _attainable(args):
     def fn(dev):
         if args.no_probes:
@@ -496,6 +614,9 @@ def main():
                     help="opt6.7b: fc1's GEMM epilogue applies ReLU and writes fc2's int8 input "
                          "codes (fc2's smoothing factor and static step), so fc2 has no "
                          "activation quantizer call; fc2's GEMM reads a static per-tensor step")
+    ap.add_argument("--alpha-sweep", action="store_true",
+                    help="ln8192: also sweep alpha over {0, .25, .5, .75, .85, 1} in static and "
+                         "per-token modes (spread, fp64 output error, clip count, GB/s, TOPS)")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the attainable-ceiling probes (MFMA loop, HBM read and copy)")
     ap.add_argument("--eager", action="store_true",
@@ -507,6 +628,9 @@ def main():
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU sharding).", file=sys.stderr)
+        sys.exit(2)
+    if args.alpha_sweep and args.workload != "ln8192":
+        print("bench.py: --alpha-sweep needs --workload ln8192", file=sys.stderr)
         sys.exit(2)
     if args.workload == "attn6.7b":
         print(json.dumps(bench_attention(args, _attainable(args))), flush=True)
@@ -753,6 +877,8 @@ def main():
     }
     if attain:
         out["attainable"] = attain
+    if args.alpha_sweep:
+        out["alpha_sweep"] = alpha_sweep(args, layers[0], dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens, w_mode, a_mode)
     print(json.dumps(out), flush=True)

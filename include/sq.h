@@ -158,7 +158,8 @@ sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T,
  *             SQ_STATIC_PER_TENSOR: static_scale [1] (device) holds dx_static;
  *             x_scale may be NULL and is not written.
  *             SQ_DYNAMIC_PER_TENSOR ([Review] §6.3 O2): x_scale [1] receives
- *             the batch step dx; static_scale is not read.
+ *             the batch step dx (also when M = 0: FLOOR / 127, so x_scale is
+ *             required for every M); static_scale is not read.
  *   xq [M, K] int8 output codes.
  * Per-token and static: one kernel that reads X once and writes xq (and
  * x_scale) once.  Dynamic per-tensor: a row-maximum pass (the maxima are

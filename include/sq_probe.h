@@ -40,6 +40,39 @@ int sqp_read(const void* src, int64_t bytes, int blocks, int* out, sqp_stream_t 
  * scales the hardware's fetched / written byte counters. */
 int sqp_copy(const void* src, void* dst, int64_t bytes, int blocks, sqp_stream_t stream);
 
+/* Exactness checks of the quantizer's short division sequences (the device
+ * functions rcp_rn, div_rn_narrow and div_rn of the library, compiled into this
+ * probe library from the same source).  Each kernel adds to counts[0] the
+ * number of results that are not the correctly rounded IEEE quotient RN(a/b)
+ * -- decided exactly from the fp64 residual a - b q, with no division
+ * instruction -- and to counts[1] the number that differ from the compiler's
+ * own IEEE division; first_bad is lowered to the smallest failing key.  The
+ * caller initialises counts (two uint64) to 0 and *first_bad to 0xffffffff.
+ * raw != 0 checks a deliberately short form instead (the negative control
+ * that shows the checker detects wrong roundings).
+ *
+ * sqp_check_rcp: every float bit pattern b in [lo, hi), 0x00800000 <= lo <
+ *   hi <= 0x7f800000; q = rcp_rn(b) (raw: the hardware estimate v_rcp_f32
+ *   alone).  Key = the bit pattern of b.
+ * sqp_check_div_narrow: all 2^30 pairs of a bf16 significand a in [1, 2) and
+ *   an fp32 significand b in [1, 2), key = a_index << 23 | b_index;
+ *   q = div_rn_narrow(a, b, rcp_rn(b)) (raw: RN(a * rcp_rn(b))).  Scaling a
+ *   or b by a power of two scales q exactly, so this covers every exponent
+ *   whose quotient stays normal.
+ * sqp_check_div: `count` pairs, b = the fp32 significand in [1, 2) with index
+ *   key mod 2^23, a an fp32 significand in [1, 2) hashed from (seed, key);
+ *   q = div_rn(a, b, rcp_rn(b)) (raw: RN(a * rcp_rn(b))). */
+int sqp_check_rcp(uint32_t lo, uint32_t hi, int raw, unsigned long long* counts,
+                  uint32_t* first_bad, sqp_stream_t stream);
+int sqp_check_div_narrow(int raw, unsigned long long* counts, uint32_t* first_bad,
+                         sqp_stream_t stream);
+int sqp_check_div(uint32_t seed, uint32_t count, int raw, unsigned long long* counts,
+                  uint32_t* first_bad, sqp_stream_t stream);
+
+/* q[i] = a[i] / b[i] with the compiler's fp32 division (n elements), so the
+ * host can confirm that division is the correctly rounded one. */
+int sqp_div_ref(const float* a, const float* b, float* q, int64_t n, sqp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -401,6 +401,10 @@ void orc_f32_to_bf16(const float* y, int64_t n, uint16_t* out) {
 
 /* ---- fp64 references ---------------------------------------------------- */
 
+/* The LayerNorm in front of a linear, LN(x) * gamma + beta ([Edge] §二), in
+ * fp64 with the biased variance: the exact-arithmetic reference of the
+ * LayerNorm workload's int8-vs-fp64 output error.  Not on the int8 path (that
+ * is orc_act_ln, fp32 with the fused kernel's order). */
 void orc_ln_f64(const void* x, int dt, int64_t M, int64_t K, const double* g, const double* b,
                 double eps, double* out) {
 #pragma omp parallel for schedule(static)

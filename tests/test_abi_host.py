@@ -106,6 +106,9 @@ def test_act_validation():
     assert _act(x=MIS) == 5
     assert _act(xq=MIS) == 5
     assert _act(M=0, x=None, xq=None, xs=None) == 0
+    # an empty batch in dynamic per-tensor mode still writes its step
+    # (FLOOR / 127) into x_scale[0]: a missing x_scale is rejected on the host
+    assert _act(M=0, mode=2, x=None, xq=None, xs=None) == 1
 
 
 def test_calibrate_validation():
@@ -162,7 +165,8 @@ def test_probe_library_exports_and_validates():
     from w8a8_int8_gemm_colwise_amd import probes
     text = open(os.path.join(ROOT, "include", "sq_probe.h")).read()
     names = set(re.findall(r"^\s*int\s+(sqp_\w+)\s*\(", text, flags=re.M))
-    assert names == {"sqp_mfma_i8", "sqp_read", "sqp_copy"}
+    assert names == {"sqp_mfma_i8", "sqp_read", "sqp_copy", "sqp_check_rcp",
+                     "sqp_check_div_narrow", "sqp_check_div", "sqp_div_ref"}
     out = subprocess.run(["nm", "-D", "--defined-only", probes.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     assert names <= set(re.findall(r" T (sqp_\w+)$", out, flags=re.M))
@@ -173,6 +177,13 @@ def test_probe_library_exports_and_validates():
     assert L.sqp_read(MIS, 64, 4, P, None) == 1           # misaligned
     assert L.sqp_copy(P, MIS, 64, 4, None) == 1
     assert L.sqp_copy(P, P + 64, 0, 4, None) == 1
+    assert L.sqp_check_rcp(0x3F800000, 0x40000000, 0, None, P, None) == 1
+    assert L.sqp_check_rcp(0x40000000, 0x3F800000, 0, P, P, None) == 1   # empty range
+    assert L.sqp_check_rcp(0x00400000, 0x3F800000, 0, P, P, None) == 1   # subnormal b
+    assert L.sqp_check_rcp(0x3F800000, 0x7F800001, 0, P, P, None) == 1   # past +inf
+    assert L.sqp_check_div_narrow(0, P, None, None) == 1
+    assert L.sqp_check_div(1, 0, 0, P, P, None) == 1
+    assert L.sqp_div_ref(P, P, P, 0, None) == 1
 
 
 def _gemm_ex(epi, ydt=0, **kw):

@@ -309,6 +309,26 @@ def test_dequant_within_two_ulps_of_exact_and_bf16_matches_torch():
     np.testing.assert_array_equal(oracle.f32_to_bf16(vals), ref)
 
 
+
+def test_dequant_order_hand_example():
+    """tests/golden/dequant_order_example.txt ([Edge] §三: the dequant factor
+    dx * dw is formed first, then (float)acc times it).  The hand-worked triple
+    separates that order from scaling by dx and then by dw by one ulp; a second
+    case pins the round-to-nearest-even int32 -> fp32 conversion."""
+    g = _golden_kv("dequant_order_example.txt")
+    u = lambda k: np.array([int(g[k][0], 16)], np.uint32).view(np.float32)
+    acc = np.array([[int(g["acc"][0])]], np.int32)
+    y = oracle.dequant(acc, u("dx_bits"), u("dw_bits"), per_token=True)
+    assert int(y.view(np.uint32)[0, 0]) == int(g["y_bits"][0], 16)
+    assert int(y.view(np.uint32)[0, 0]) != int(g["y_bits_other_order"][0], 16)
+    yt = oracle.dequant(acc, u("dx_bits"), u("dw_bits"), per_token=False, w_per_tensor=True)
+    assert int(yt.view(np.uint32)[0, 0]) == int(g["y_bits"][0], 16)
+    one = np.ones(1, np.float32)
+    y2 = oracle.dequant(np.array([[int(g["acc2"][0]), -int(g["acc2"][0])]], np.int32), one,
+                        np.ones(2, np.float32), per_token=True)
+    assert y2[0, 0] == np.float32(float(g["y2"][0])) and y2[0, 1] == -np.float32(float(g["y2"][0]))
+
+
 # ---- LayerNorm mode ---------------------------------------------------------------
 
 def test_canonical_sum_hand_cases():
@@ -350,6 +370,49 @@ def test_layernorm_fold_against_fp64_layernorm():
     assert np.all(np.abs(xh - ref) <= 4e-6 * scale)
     # rows selection consistent
     np.testing.assert_array_equal(oracle.act_ln(x, gs, bs, rows=[5, 1]), xh[[5, 1]])
+
+
+
+def test_ln_f64_closed_forms():
+    """The fp64 LayerNorm reference (the denominator of the LayerNorm
+    workload's int8-vs-fp64 error, [Edge] §二 LN(x) * gamma + beta) on rows
+    whose mean and biased variance are known by construction:
+      - a constant row has d = 0, so the output is beta exactly;
+      - a row alternating c + a, c - a has mean c and biased variance a^2, so
+        channel k gives +-a / sqrt(a^2 + eps) * gamma_k + beta_k (the unbiased
+        variance would give a^2 K / (K - 1); a swapped sign or a transposed
+        gamma / beta fails the per-channel values).
+    The same rows stored as bf16 (values exact in 8 bits) give the same result."""
+    K = 8
+    rng = np.random.default_rng(21)
+    gamma = rng.uniform(0.5, 1.5, K)
+    beta = rng.normal(0, 0.3, K)
+    eps = 1e-5
+    c, a = 3.0, 2.0
+    sign = np.array([1.0, -1.0] * (K // 2))
+    rows = np.stack([np.full(K, 5.25), c + a * sign]).astype(np.float32)
+    out = oracle.ln_f64(rows, gamma, beta, eps)
+    assert np.array_equal(out[0], beta)
+    want = sign * (a / np.sqrt(a * a + eps)) * gamma + beta
+    assert np.allclose(out[1], want, rtol=1e-14, atol=1e-14)
+    unbiased = sign * (a / np.sqrt(a * a * K / (K - 1) + eps)) * gamma + beta
+    assert not np.allclose(out[1], unbiased, rtol=1e-6, atol=1e-6)
+    bits = (rows.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_to_f32(bits), rows)
+    np.testing.assert_array_equal(oracle.ln_f64(bits, gamma, beta, eps), out)
+
+
+def test_ln_f64_matches_fp32_layernorm_to_its_rounding():
+    """The fp32 LayerNorm of the fused kernel's contract (canonical sums, one
+    rounding per operation) stays within a few fp32 ulps of the fp64 one on
+    the LayerNorm workload's tokens, with gamma and beta unfolded (s = 1)."""
+    spec = datagen.workload(5).layers[0]
+    x = datagen.eval_x(spec, M=8)
+    gamma, beta = datagen.ln_params(spec)
+    ref = oracle.ln_f64(x, gamma.astype(np.float64), beta.astype(np.float64), 1e-5)
+    got = oracle.act_ln(x, gamma, beta, eps=1e-5)
+    scale = np.abs(ref).max(axis=1, keepdims=True)
+    assert np.all(np.abs(got - ref) <= 4e-6 * scale)
 
 
 # ---- whole path: eq. (3) and error bounds -------------------------------------------

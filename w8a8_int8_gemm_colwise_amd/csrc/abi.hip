@@ -96,7 +96,10 @@ sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_
     }
     if (mode == SQ_STATIC_PER_TENSOR && !static_scale) return SQ_ERR_NULL_ARG;
     if (M > 0 && (!x || !xq)) return SQ_ERR_NULL_ARG;
-    if (M > 0 && mode != SQ_STATIC_PER_TENSOR && !x_scale) return SQ_ERR_NULL_ARG;
+    // per-token steps are written only for rows that exist; the batch step of
+    // the dynamic per-tensor mode is written even for an empty batch (FLOOR/127)
+    if (mode == SQ_PER_TOKEN && M > 0 && !x_scale) return SQ_ERR_NULL_ARG;
+    if (mode == SQ_DYNAMIC_PER_TENSOR && !x_scale) return SQ_ERR_NULL_ARG;
     const float* st = (mode == SQ_STATIC_PER_TENSOR) ? static_scale : nullptr;
     const void* ptrs[] = {x, s, ln_gamma_s, ln_beta_s, st, xq, x_scale};
     for (const void* p : ptrs)

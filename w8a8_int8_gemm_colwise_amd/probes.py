@@ -32,7 +32,13 @@ def lib():
                                ctypes.c_void_p]
         L.sqp_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                ctypes.c_void_p]
-        for f in (L.sqp_mfma_i8, L.sqp_read, L.sqp_copy):
+        vp, u32, i64, ci = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int
+        L.sqp_check_rcp.argtypes = [u32, u32, ci, vp, vp, vp]
+        L.sqp_check_div_narrow.argtypes = [ci, vp, vp, vp]
+        L.sqp_check_div.argtypes = [u32, u32, ci, vp, vp, vp]
+        L.sqp_div_ref.argtypes = [vp, vp, vp, i64, vp]
+        for f in (L.sqp_mfma_i8, L.sqp_read, L.sqp_copy, L.sqp_check_rcp, L.sqp_check_div_narrow,
+                  L.sqp_check_div, L.sqp_div_ref):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -110,3 +116,51 @@ def hbm_copy_gbs(dev, nbytes: int = 512 << 20, blocks: int = 2048, reps: int = 5
     stream = torch.cuda.current_stream(dev)
     ms = _best_ms(torch, stream, lambda: copy(dev, src, dst, nbytes, blocks), reps)
     return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+# ---- exactness checks of the library's short division sequences ---------------
+
+def _run_check(dev, launch):
+    """Run one check kernel; returns (not correctly rounded, differs from the
+    compiler's IEEE division, smallest failing key or None)."""
+    import torch
+    counts = torch.zeros(2, dtype=torch.int64, device=dev)
+    first = torch.full((1,), -1, dtype=torch.int32, device=dev)  # 0xffffffff
+    stream = torch.cuda.current_stream(dev)
+    launch(counts.data_ptr(), first.data_ptr(), stream.cuda_stream)
+    torch.cuda.synchronize(dev)
+    c = counts.cpu().tolist()
+    f = int(first.cpu().numpy().view(np.uint32)[0])
+    return c[0], c[1], (None if f == 0xFFFFFFFF else f)
+
+
+def check_rcp(dev, lo: int, hi: int, raw: bool = False):
+    """rcp_rn(b) for every float bit pattern b in [lo, hi) (sq_probe.h)."""
+    L = lib()
+    return _run_check(dev, lambda c, f, s: _check(L.sqp_check_rcp(lo, hi, int(raw), c, f, s),
+                                                  "sqp_check_rcp"))
+
+
+def check_div_narrow(dev, raw: bool = False):
+    """div_rn_narrow over every bf16 x fp32 significand pair (sq_probe.h)."""
+    L = lib()
+    return _run_check(dev, lambda c, f, s: _check(L.sqp_check_div_narrow(int(raw), c, f, s),
+                                                  "sqp_check_div_narrow"))
+
+
+def check_div(dev, seed: int, count: int, raw: bool = False):
+    """div_rn on `count` hashed fp32 significand pairs (sq_probe.h)."""
+    L = lib()
+    return _run_check(dev, lambda c, f, s: _check(L.sqp_check_div(seed, count, int(raw), c, f, s),
+                                                  "sqp_check_div"))
+
+
+def div_ref(dev, a, b):
+    """The compiler's fp32 division a / b on the GPU (torch float32 tensors)."""
+    import torch
+    q = torch.empty_like(a)
+    stream = torch.cuda.current_stream(dev)
+    _check(lib().sqp_div_ref(a.data_ptr(), b.data_ptr(), q.data_ptr(), a.numel(),
+                             stream.cuda_stream), "sqp_div_ref")
+    torch.cuda.synchronize(dev)
+    return q
