@@ -69,9 +69,10 @@ extern "C" {
 
 typedef struct ihipStream_t* sq_stream_t; /* a hipStream_t */
 
-#define SQ_ABI_VERSION 3
+#define SQ_ABI_VERSION 4
 #define SQ_MAX_K 133120          /* largest multiple of 64 with 127*127*K < 2^31 */
 #define SQ_ABSMAX_FLOOR 1e-7f    /* floor of every absolute maximum */
+#define SQ_NOALLOC_MAX_K 16384   /* largest K of sq_channel_quantile_noalloc */
 
 typedef enum {
     SQ_OK = 0,
@@ -276,6 +277,23 @@ size_t sq_channel_quantile_workspace_size(int64_t K);
 sq_status sq_channel_quantile(const void* x, sq_dtype x_dt, int64_t T, int64_t K, float q,
                               float* out, void* workspace, size_t workspace_bytes,
                               sq_stream_t stream);
+
+/*
+ * sq_channel_quantile_noalloc -- sq_channel_quantile for callers that cannot
+ *   allocate device memory (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid hipMalloc): no workspace argument, and the call
+ *   allocates nothing.  The histogram and rank words live in a scratch array
+ *   the library holds on every device it runs on, from module load until the
+ *   process ends: SQ_NOALLOC_MAX_K * 1032 + 256 bytes (about 16 MiB), so K
+ *   must not exceed SQ_NOALLOC_MAX_K (else SQ_ERR_BAD_SHAPE).  Every other
+ *   argument, the result and the errors are those of sq_channel_quantile.  The
+ *   stream must belong to the current device.  All calls on one device share
+ *   its array (each call clears what it uses, so earlier contents never
+ *   matter): calls that overlap on one device -- on different streams, or
+ *   from different host threads -- race and give undefined results.
+ */
+sq_status sq_channel_quantile_noalloc(const void* x, sq_dtype x_dt, int64_t T, int64_t K,
+                                      float q, float* out, sq_stream_t stream);
 
 /*
  * sq_calibrate_stat -- sq_calibrate with a given per-channel activation

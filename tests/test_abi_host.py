@@ -234,6 +234,24 @@ def test_bmm_validation():
     assert _bmm(batch=0, xq=None, wq=None, y=None) == 0
 
 
+def test_noalloc_quantile_validation():
+    """sq_channel_quantile_noalloc rejects K above SQ_NOALLOC_MAX_K, a missing
+    or misaligned pointer and q outside (0, 1] before any launch."""
+    L = sq.lib()
+    f = lambda T=8, K=64, x=P, dt=1, q=0.5, out=P: L.sq_channel_quantile_noalloc(
+        x, dt, T, K, q, out, None)
+    assert f(K=sq.SQ_NOALLOC_MAX_K + 64) == 2
+    assert f(K=96) == 2
+    assert f(T=-1) == 2
+    assert f(dt=2) == 3
+    assert f(q=0.0) == 7
+    assert f(q=1.5) == 7
+    assert f(out=None) == 1
+    assert f(x=None) == 1
+    assert f(x=MIS) == 5
+    assert f(out=MIS) == 5
+
+
 def test_robust_calibration_validation():
     """Channel quantile, calibration from a statistic, clip count and alpha
     search reject bad arguments (and a short workspace) before any device work."""

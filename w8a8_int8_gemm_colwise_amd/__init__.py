@@ -15,6 +15,7 @@ functions carry the C ABI's names (include/sq.h):
                           codes for the next linear)
   sq_bmm_w8a8             batched int8 GEMM (the attention products)
   sq_channel_quantile     robust per-channel activation statistic
+  sq_channel_quantile_noalloc  the same without a workspace (no allocation)
   sq_calibrate_stat       the offline half from a given activation statistic
   sq_clip_count           saturation count of the static quantizer
   sq_alpha_search         candidate alphas: output and weight errors
@@ -36,7 +37,8 @@ SQ_F32, SQ_BF16, SQ_I8, SQ_I32 = 0, 1, 2, 3
 SQ_PER_TOKEN, SQ_STATIC_PER_TENSOR, SQ_DYNAMIC_PER_TENSOR = 0, 1, 2
 SQ_W_PER_CHANNEL, SQ_W_PER_TENSOR = 0, 1
 SQ_MAX_K = 133120
-SQ_ABI_VERSION = 3
+SQ_ABI_VERSION = 4
+SQ_NOALLOC_MAX_K = 16384
 
 # The SmoothQuant efficiency levels ([Review] §6.3): (weight mode, activation
 # mode).  "colwise" is the per-output-channel weight path with per-token
@@ -49,7 +51,8 @@ SETTINGS = {
 }
 EXPORTED = ("sq_calibrate", "sq_smooth_quantize_act", "sq_gemm_w8a8", "sq_gemm_w8a8_ex",
             "sq_bmm_w8a8", "sq_channel_quantile_workspace_size", "sq_channel_quantile",
-            "sq_calibrate_stat", "sq_clip_count", "sq_alpha_search_workspace_size",
+            "sq_channel_quantile_noalloc", "sq_calibrate_stat", "sq_clip_count",
+            "sq_alpha_search_workspace_size",
             "sq_alpha_search", "sq_status_string", "sq_abi_version")
 
 
@@ -94,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.sq_channel_quantile_workspace_size.argtypes = [i64]
     L.sq_channel_quantile.restype = ci
     L.sq_channel_quantile.argtypes = [vp, ci, i64, i64, cf, vp, vp, sz, vp]
+    L.sq_channel_quantile_noalloc.restype = ci
+    L.sq_channel_quantile_noalloc.argtypes = [vp, ci, i64, i64, cf, vp, vp]
     L.sq_calibrate_stat.restype = ci
     L.sq_calibrate_stat.argtypes = [vp, vp, ci, i64, i64, cf, ci, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, vp, vp]
@@ -385,6 +390,18 @@ def sq_channel_quantile(x: torch.Tensor, q: float, out: torch.Tensor | None = No
         _vec(out, K, "out", x.device)
     _check(lib().sq_channel_quantile(_ptr(x), _dt(x), T, K, float(q), _ptr(out), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(x.device)))
+    return out
+
+
+def sq_channel_quantile_noalloc(x: torch.Tensor, q: float, out: torch.Tensor) -> torch.Tensor:
+    """sq_channel_quantile without a workspace (the library's own per-device
+    scratch; K <= SQ_NOALLOC_MAX_K): for callers that cannot allocate, so the
+    output ``out`` (fp32 [K]) is required."""
+    _dev2d(x, "x")
+    T, K = x.shape
+    _vec(out, K, "out", x.device)
+    _check(lib().sq_channel_quantile_noalloc(_ptr(x), _dt(x), T, K, float(q), _ptr(out),
+                                             _stream(x.device)))
     return out
 
 

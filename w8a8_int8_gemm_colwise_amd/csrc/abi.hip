@@ -212,6 +212,20 @@ sq_status sq_channel_quantile(const void* x, sq_dtype x_dt, int64_t T, int64_t K
                                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
+sq_status sq_channel_quantile_noalloc(const void* x, sq_dtype x_dt, int64_t T, int64_t K,
+                                      float q, float* out, sq_stream_t stream) {
+    if (!valid_k(K) || !valid_rows(T) || K > SQ_NOALLOC_MAX_K) return SQ_ERR_BAD_SHAPE;
+    if (!float_dtype(x_dt)) return SQ_ERR_BAD_DTYPE;
+    if (!(q > 0.0f && q <= 1.0f)) return SQ_ERR_BAD_MODE;
+    if (!out || (T > 0 && !x)) return SQ_ERR_NULL_ARG;
+    if (!aligned16(x) || !aligned16(out)) return SQ_ERR_ALIGNMENT;
+    const int64_t r = std::max<int64_t>(
+        1, std::min<int64_t>(T, static_cast<int64_t>(std::ceil(static_cast<double>(q) *
+                                                               static_cast<double>(T)))));
+    return from_hip(sq::launch_channel_quantile_noalloc(x, to_dt(x_dt), T, K, r, out,
+                                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 sq_status sq_clip_count(const void* x, sq_dtype x_dt, int64_t M, int64_t K, const float* s,
                         const float* ln_gamma_s, const float* ln_beta_s, float ln_eps,
                         const float* static_scale, unsigned long long* count,

@@ -26,7 +26,9 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
+#include "../../include/sq.h"
 #include "sq_device.hpp"
 #include "sq_internal.hpp"
 
@@ -463,8 +465,51 @@ AlphaWs carve(void* base, int64_t T, int64_t N, int64_t K) {
 
 }  // namespace
 
-size_t quantile_workspace_bytes(int64_t K) {
+constexpr size_t quantile_ws_bytes(int64_t K) {
     return static_cast<size_t>(K) * (kQBins * 4 + 8) + 256;
+}
+
+size_t quantile_workspace_bytes(int64_t K) { return quantile_ws_bytes(K); }
+
+// ---- the channel quantile without a caller workspace ---------------------------
+//
+// For callers that cannot allocate device memory: the quantile's histogram,
+// prefix and rank words live in this file-scope array instead of a caller
+// workspace (every device the library runs on holds its own copy from module
+// load until the process ends).  Its host-side name is not a device address:
+// each device's address is looked up once, with that device current, and only
+// that address is passed to the kernels.  quantile_init_kernel clears the
+// words each call, so the previous call's contents never matter; calls that
+// overlap on one device share the array and race.
+constexpr size_t kNoAllocBytes = quantile_ws_bytes(SQ_NOALLOC_MAX_K);
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};  // each device's address of `scratch`
+}  // namespace
+
+hipError_t launch_channel_quantile_noalloc(const void* x, Dt x_dt, int64_t T, int64_t K,
+                                           int64_t rank, float* out, hipStream_t stream) {
+    if (quantile_ws_bytes(K) > kNoAllocBytes) return hipErrorInvalidValue;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (g_scratch[dev] == nullptr) {
+            void* p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch[dev] = p;
+        }
+        ws = g_scratch[dev];
+    }
+    return launch_channel_quantile(x, x_dt, T, K, rank, out, ws, stream);
 }
 
 hipError_t launch_channel_quantile(const void* x, Dt x_dt, int64_t T, int64_t K, int64_t rank,

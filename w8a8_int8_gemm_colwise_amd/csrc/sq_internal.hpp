@@ -35,6 +35,10 @@ hipError_t launch_clip_count(const void* x, Dt x_dt, int64_t M, int64_t K, const
 size_t quantile_workspace_bytes(int64_t K);
 hipError_t launch_channel_quantile(const void* x, Dt x_dt, int64_t T, int64_t K, int64_t rank,
                                    float* out, void* ws, hipStream_t stream);
+// The same with the library's own per-device scratch (K <= SQ_NOALLOC_MAX_K;
+// the current device must be the stream's): no allocation, no workspace.
+hipError_t launch_channel_quantile_noalloc(const void* x, Dt x_dt, int64_t T, int64_t K,
+                                           int64_t rank, float* out, hipStream_t stream);
 
 // Activation smoothing + quantization (runtime).
 hipError_t launch_act_quant(const void* x, Dt x_dt, int64_t M, int64_t K, const float* s,
