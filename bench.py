@@ -810,8 +810,15 @@ def main():
         }
     value = tot_ops / (ms_per_step * 1e-3) / 1e12
 
-    # attainable ceilings on this machine (after the timed region)
+    # attainable ceilings on this machine (after the timed region), and the
+    # int8 GEMM shipped with PyTorch-ROCm on the same shapes (a reference point)
     attain = _attainable(args)(dev)
+    if attain and not all(L["M"] <= 64 for L in layers):
+        from w8a8_int8_gemm_colwise_amd import probes
+        attain["vendor_int8_gemm_TOPS"] = probes.vendor_int8_gemm_tops(
+            dev, [(L["M"], L["spec"].N, L["spec"].K) for L in layers])
+        attain["vendor_int8_gemm_how"] = ("torch._int_mm (int32 output, weight passed "
+                                          "transposed), best of 10 cold calls")
 
     # dominant kernel by time: the GEMM unless the HBM-bound calls take longer
     tg, tc, ta = t_gemm.sum(), t_cal.sum(), t_act.sum()

@@ -138,6 +138,29 @@ __device__ __forceinline__ int code_of(float q) {
     return static_cast<int>(r);
 }
 
+// rne of a quotient |q| < 2^22, with the int8 code in the low byte of the
+// result: q + 1.5 * 2^23 lands in [2^23, 2^24), where the fp32 spacing is 1, so
+// the addition itself rounds q to the nearest integer (ties to even, the
+// default rounding mode), and the low bits of the sum's bit pattern hold that
+// integer in two's complement (the bit pattern of 1.5 * 2^23 ends in 22 zero
+// bits).  CLAMP: the quotient is first clamped to [-127, 127], which equals
+// clamping the rounded value; without it the caller guarantees |q| < 127.5.
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t code_bits(float q) {
+    if (CLAMP) q = __builtin_amdgcn_fmed3f(q, -kQmax, kQmax);
+    return __float_as_uint(q + 12582912.0f);
+}
+
+// Pack the low bytes of 8 words from code_bits (byte i = element i).
+__device__ __forceinline__ uint2 pack8_bits(const uint32_t (&b)[kChunk]) {
+    const uint32_t p01 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+    const uint32_t p45 = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u);
+    const uint32_t p67 = __builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u);
+    return make_uint2(__builtin_amdgcn_perm(p23, p01, 0x05040100u),
+                      __builtin_amdgcn_perm(p67, p45, 0x05040100u));
+}
+
 // Pack 8 codes into two 32-bit words (byte i = element i).
 __device__ __forceinline__ uint2 pack8(const int (&c)[kChunk]) {
     uint32_t lo = (c[0] & 0xff) | ((c[1] & 0xff) << 8) | ((c[2] & 0xff) << 16) |

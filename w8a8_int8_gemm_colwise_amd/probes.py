@@ -118,6 +118,40 @@ def hbm_copy_gbs(dev, nbytes: int = 512 << 20, blocks: int = 2048, reps: int = 5
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def vendor_int8_gemm_tops(dev, shapes, reps: int = 10, seed: int = 11) -> dict:
+    """Reference point only (not on the path): the int8 GEMM that ships with
+    PyTorch-ROCm (torch._int_mm, int32 output) on the given (M, N, K) shapes,
+    with the weight [N, K] passed transposed (the same K-contiguous operands as
+    the library's), a 512 MiB write between timed calls; best of ``reps``."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for M, N, K in shapes:
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, generator=g).to(dev)
+        w = torch.randint(-127, 128, (N, K), dtype=torch.int8, generator=g).to(dev)
+        try:
+            torch._int_mm(a, w.t())
+        except RuntimeError as ex:  # not available in this build
+            out[f"{M}x{N}x{K}"] = f"unavailable: {ex}"
+            continue
+        torch.cuda.synchronize(dev)
+        best = float("inf")
+        for r in range(reps):
+            flush.fill_(r & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            torch._int_mm(a, w.t())
+            e1.record(stream)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        out[f"{M}x{N}x{K}"] = round(2.0 * M * N * K / (best * 1e-3) / 1e12, 1)
+        del a, w
+    return out
+
+
 # ---- exactness checks of the library's short division sequences ---------------
 
 def _run_check(dev, launch):
