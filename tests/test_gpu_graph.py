@@ -75,3 +75,50 @@ def test_graph_replays_match_eager():
             assert torch.equal(g, e), f"replay {r}: output {i} differs from the eager step"
         _step([other])               # eager library work between the replays
         torch.cuda.synchronize()
+
+
+def _step_two_streams(layers, side):
+    """Calibrations on `side` in order, each linear's quantizer and GEMM on the
+    current stream after an event of its own calibration (fork at the start,
+    join at the end) -- the overlapped step of the benchmark."""
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    done, cals = [], []
+    with torch.cuda.stream(side):
+        for L in layers:
+            cals.append(sq.sq_calibrate(L["xc"], L["w"], L["alpha"], out=L["cal"]))
+            e = torch.cuda.Event()
+            e.record(side)
+            done.append(e)
+    for L, cal, e in zip(layers, cals, done):
+        main.wait_event(e)
+        sq.sq_smooth_quantize_act(L["x"], cal["s"], xq=L["xq"], x_scale=L["xs"])
+        sq.sq_gemm_w8a8(L["xq"], L["xs"], cal["wq"], cal["w_scale"], y=L["y"])
+    main.wait_stream(side)
+
+
+def test_graph_two_streams_replays_match_eager():
+    d = dev()
+    # GEMMs large enough to keep every CU busy while the later calibrations run
+    layers = [_layer(d, 2048, 4096, 2048, 11), _layer(d, 2048, 2048, 4096, 12),
+              _layer(d, 1024, 3072, 1024, 13), _layer(d, 300, 512, 1024, 14)]
+    _step(layers)
+    torch.cuda.synchronize()
+    ref = _outputs(layers)
+    side = torch.cuda.Stream(d)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _step_two_streams(layers, side)
+    torch.cuda.synchronize()
+    other = _layer(d, 130, 192, 256, 4)
+    for r in range(4):
+        _clear(layers)
+        torch.cuda.synchronize()
+        say(f"[case] two-stream graph replay {r}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _outputs(layers)
+        for i, (g, e) in enumerate(zip(got, ref)):
+            assert torch.equal(g, e), f"replay {r}: output {i} differs from the eager step"
+        _step([other])
+        torch.cuda.synchronize()
