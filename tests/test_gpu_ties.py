@@ -1,7 +1,7 @@
 """Exact quantizer ties on the GPU, every element against the oracle.
 
 [Review] §2.2 rounds x / Delta to the nearest integer without fixing the tie
-rule; this build rounds half to even (the [Edge] §三 listing's roundf rounds
+rule; the library and the oracle round half to even (the [Edge] §三 listing's roundf rounds
 half away from zero, and the two differ exactly at x / Delta = k + 1/2).
 Random workload data almost never lands on a tie, so these inputs are built
 to: steps that are powers of two (or 1.5 times one), smoothing factors that

@@ -133,7 +133,7 @@ def vendor_int8_gemm_tops(dev, shapes, reps: int = 10, seed: int = 11) -> dict:
         w = torch.randint(-127, 128, (N, K), dtype=torch.int8, generator=g).to(dev)
         try:
             torch._int_mm(a, w.t())
-        except RuntimeError as ex:  # not available in this build
+        except RuntimeError as ex:  # not available in this PyTorch
             out[f"{M}x{N}x{K}"] = f"unavailable: {ex}"
             continue
         torch.cuda.synchronize(dev)
