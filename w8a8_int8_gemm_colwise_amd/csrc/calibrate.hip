@@ -353,7 +353,7 @@ template <typename T, int CPT, int D, int MAXT = 1024, int WM = kWChannel>
 __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
     const T* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,
     int8_t* __restrict__ wq, float* __restrict__ w_scale) {
-    __shared__ float red[16];
+    __shared__ float red[2][16];  // alternate rows use alternate halves: one barrier per row
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
     const int nw = nthr >> 6;
@@ -383,7 +383,8 @@ __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
             if (c < chunks) load_chunk(s, c, sv[CACHE ? i : 0]);
         }
     }
-    for (int64_t n = blockIdx.x; n < N; n += G) {
+    int parity = 0;
+    for (int64_t n = blockIdx.x; n < N; n += G, parity ^= 1) {
         if (n + D * G < N) fetch(n + D * G, ring[D]);
         float v[CPT][kChunk];
         float m = 0.0f;
@@ -410,25 +411,31 @@ __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
         if (WM != kWGiven) {
             m = wave_max(m);
             if (nw > 1) {
-                if ((tid & 63) == 0) red[tid >> 6] = m;
+                // the next row writes the other half of red, and the row after
+                // it passes this row's successor's barrier first, which every
+                // wave reaches only after reading this half
+                if ((tid & 63) == 0) red[parity][tid >> 6] = m;
                 __syncthreads();
-                m = red[0];
-                for (int i = 1; i < nw; ++i) m = fmaxf(m, red[i]);
-                __syncthreads();  // red is reused by the next row
+                m = red[parity][0];
+                for (int i = 1; i < nw; ++i) m = fmaxf(m, red[parity][i]);
             }
             d = step_from_absmax(m);
             rd = 1.0f / d;
             if (tid == 0) w_scale[n] = d;
         }
+        // the step comes from the row's maximum (or, given, from the tensor's,
+        // which bounds every row): d = RN(max(FLOOR, m) / 127) >= m / 127 (1 - 2^-24),
+        // so every quotient is at most 127.00001 in magnitude and the clamp of
+        // the code cannot act: the code is taken without it (code_bits)
         int8_t* orow = wq + n * K;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int64_t c = tid + static_cast<int64_t>(i) * nthr;
             if (c < chunks) {
-                int q[kChunk];
+                uint32_t q[kChunk];
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) q[e] = code_of(div_rn(v[i][e], d, rd));
-                *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8(q);
+                for (int e = 0; e < kChunk; ++e) q[e] = code_bits<false>(div_rn(v[i][e], d, rd));
+                *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8_bits(q);
             }
         }
 #pragma unroll
@@ -472,10 +479,10 @@ __global__ __launch_bounds__(256) void weight_quant_stream_kernel(
             float v[kChunk], sv[kChunk];
             load_chunk(row, c, v);
             load_chunk(s, c, sv);
-            int q[kChunk];
+            uint32_t q[kChunk];  // no clamp needed, as in weight_quant_kernel
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) q[e] = code_of(div_rn(v[e] * sv[e], d, rd));
-            *reinterpret_cast<uint2*>(wq + n * K + c * kChunk) = pack8(q);
+            for (int e = 0; e < kChunk; ++e) q[e] = code_bits<false>(div_rn(v[e] * sv[e], d, rd));
+            *reinterpret_cast<uint2*>(wq + n * K + c * kChunk) = pack8_bits(q);
         }
     }
 }
