@@ -23,6 +23,9 @@
 // per-element arithmetic and have a row-maximum pass (the first pass of the
 // dynamic per-tensor step) and a count mode (the static quantizer's
 // saturation count, no codes written).
+// act_quant_multi_kernel (plain) and act_quant_ln2_kernel (LayerNorm) take two
+// bf16 rows per block; act_quant_static_stream_kernel maps long rows
+// elementwise when the step is per tensor.  Same arithmetic per element.
 #include <algorithm>
 
 #include "sq_device.hpp"
