@@ -29,6 +29,7 @@ CASES = [
     (33, 200, 512, "bf16", "bf16", True),        # skinny GEMM, two 32-row tiles, LN
     (1, 33, 256, "f32", "f32", True),
     (5, 96, 24576, "bf16", "bf16", False),
+    (40, 700, 16384, "bf16", "f32", False),      # per-tensor weight step: elementwise map
     (4, 40, 133120, "bf16", "bf16", False),      # two-sweep weight and activation kernels
     (70, 130, 8192, "bf16", "bf16", True),
 ]

@@ -487,11 +487,59 @@ __global__ __launch_bounds__(256) void weight_quant_stream_kernel(
     }
 }
 
+// Given (per-tensor) step: each code depends only on W[n,k], s_k and the step,
+// so long rows are mapped elementwise.  Block b covers column segment
+// b % segs (NT chunks, one per lane, s in registers) over row group b / segs,
+// RU rows' loads in flight per lane.  Same arithmetic as weight_quant_kernel.
+template <typename T, int NT, int RU>
+__global__ __launch_bounds__(NT) void weight_quant_given_stream_kernel(
+    const T* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,
+    int8_t* __restrict__ wq, const float* __restrict__ w_scale, int segs, int64_t rpb) {
+    const int64_t chunks = K / kChunk;
+    const int64_t seg = blockIdx.x % segs, rg = blockIdx.x / segs;
+    const int64_t c = seg * NT + threadIdx.x;
+    const int64_t r0 = rg * rpb, r1 = min(N, r0 + rpb);
+    if (c >= chunks || r0 >= N) return;
+    float sv[kChunk];
+    load_chunk(s, c, sv);
+    const float d = w_scale[0];
+    const float rd = 1.0f / d;
+    for (int64_t n = r0; n < r1; n += RU) {
+        RawChunk<T> raw[RU];
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+            if (n + u < r1) raw[u] = load_raw(w + (n + u) * K, c);
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            if (n + u < r1) {
+                float v[kChunk];
+                unpack(raw[u], v);
+                uint32_t q[kChunk];  // the tensor's step bounds every quotient (no clamp)
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) q[e] = code_bits<false>(div_rn(v[e] * sv[e], d, rd));
+                *reinterpret_cast<uint2*>(wq + (n + u) * K + c * kChunk) = pack8_bits(q);
+            }
+        }
+    }
+}
+
 template <typename T, int WM>
 hipError_t launch_weight_quant_mode(const T* w, int64_t N, int64_t K, const float* s, int8_t* wq,
                                     float* ws, hipStream_t stream) {
     if (N <= 0) return hipSuccess;
     const int64_t chunks = K / kChunk;
+    if (WM == kWGiven && chunks >= 2048) {
+        // rows of 16384 elements or more with the per-tensor step: elementwise,
+        // about 4096 blocks of 256 lanes (as the activation side's per-tensor map)
+        constexpr int NT = 256, RU = 4;
+        const int segs = static_cast<int>((chunks + NT - 1) / NT);
+        const int64_t groups = std::max<int64_t>(1, std::min<int64_t>((N + RU - 1) / RU, 4096 / segs));
+        const int64_t rpb = (N + groups - 1) / groups;
+        const int64_t nblk = static_cast<int64_t>(segs) * ((N + rpb - 1) / rpb);
+        weight_quant_given_stream_kernel<T, NT, RU><<<static_cast<unsigned>(nblk), NT, 0, stream>>>(
+            w, N, K, s, wq, ws, segs, rpb);
+        return hipGetLastError();
+    }
     // Measured on the MI355X: one prefetched row (D = 1) beats deeper rings, and
     // bf16 rows stream best with four 16-byte loads per lane (fp32 rows with
     // two, which keeps the prefetch ring within the register budget).  Rows
