@@ -486,6 +486,52 @@ __global__ __launch_bounds__(NT) void act_quant_static_stream_kernel(
     }
 }
 
+// Plain mode, the first pass of the dynamic per-tensor step on long rows: the
+// largest |RN(x / s_k)| of the whole batch needs no row structure either.  The
+// column-segment layout of act_quant_static_stream_kernel; each block leaves
+// its maximum in partial[blockIdx.x] for the one-block reduction.
+template <typename T, int NT, int RU>
+__global__ __launch_bounds__(NT) void act_absmax_stream_kernel(
+    const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
+    float* __restrict__ partial, int segs, int64_t rpb) {
+    __shared__ float red[NT / 64];
+    const int tid = threadIdx.x;
+    const int64_t chunks = K / kChunk;
+    const int64_t seg = blockIdx.x % segs, rg = blockIdx.x / segs;
+    const int64_t c = seg * NT + tid;
+    const bool ok = c < chunks;
+    const int64_t cc = ok ? c : chunks - 1;  // idle lanes read a valid chunk, count nothing
+    const int64_t r0 = rg * rpb, r1 = min(M, r0 + rpb);
+    float sv[kChunk], rs[kChunk];
+    load_chunk(s, cc, sv);
+    rcp_chunk(sv, rs);
+    float mx = 0.0f;
+    for (int64_t m = r0; m < r1; m += RU) {
+        RawChunk<T> raw[RU];
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+            if (m + u < r1) raw[u] = load_raw(x + (m + u) * K, cc);
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            if (ok && m + u < r1) {
+                float v[kChunk];
+                unpack(raw[u], v);
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) mx = fmaxf(mx, fabsf(div_x<T>(v[e], sv[e], rs[e])));
+            }
+        }
+    }
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    if (tid == 0) {
+        float m = red[0];
+#pragma unroll
+        for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+        partial[blockIdx.x] = m;
+    }
+}
+
 // LayerNorm mode, two rows at once (codes of the per-token or static
 // quantizer): exactly 256 lanes, so lane t owns canonical partial t of both
 // rows; the cached gamma'_k and beta'_k serve both rows, each of the three
@@ -1057,12 +1103,32 @@ hipError_t launch_act_quant(const void* x, Dt x_dt, int64_t M, int64_t K, const 
         return go(ActArgs{x, M, K, s, gamma_s, beta_s, eps, static_scale, xq, x_scale, nullptr},
                   mode == ActMode::Static);
     // dynamic per tensor: row maxima (staged in xq, 4M <= M*K bytes), the
-    // one-block reduction into x_scale[0], then the static quantizer with it
+    // one-block reduction into x_scale[0], then the static quantizer with it.
+    // Plain rows of 2048 elements or more: block maxima of the streaming pass
+    // instead of row maxima (at most segs * M floats with segs = ceil(K / 2048),
+    // so they fit in xq's M * K bytes as well)
     float* rowmax = reinterpret_cast<float*>(xq);
-    hipError_t e = go(ActArgs{x, M, K, s, gamma_s, beta_s, eps, nullptr, xq, nullptr, rowmax},
-                      false);
+    const int64_t chunks = K / kChunk;
+    hipError_t e;
+    int64_t nmax = M;
+    if (!ln && chunks >= 256) {
+        constexpr int NT = 256, RU = 4;
+        const int segs = static_cast<int>((chunks + NT - 1) / NT);
+        const int64_t groups = std::max<int64_t>(1, std::min<int64_t>((M + RU - 1) / RU, 4096 / segs));
+        const int64_t rpb = (M + groups - 1) / groups;
+        nmax = static_cast<int64_t>(segs) * ((M + rpb - 1) / rpb);
+        if (x_dt == Dt::BF16)
+            act_absmax_stream_kernel<uint16_t, NT, RU><<<static_cast<unsigned>(nmax), NT, 0, stream>>>(
+                static_cast<const uint16_t*>(x), M, K, s, rowmax, segs, rpb);
+        else
+            act_absmax_stream_kernel<float, NT, RU><<<static_cast<unsigned>(nmax), NT, 0, stream>>>(
+                static_cast<const float*>(x), M, K, s, rowmax, segs, rpb);
+        e = hipGetLastError();
+    } else {
+        e = go(ActArgs{x, M, K, s, gamma_s, beta_s, eps, nullptr, xq, nullptr, rowmax}, false);
+    }
     if (e != hipSuccess) return e;
-    e = launch_tensor_step(rowmax, M, x_scale, stream);
+    e = launch_tensor_step(rowmax, nmax, x_scale, stream);
     if (e != hipSuccess) return e;
     return go(ActArgs{x, M, K, s, gamma_s, beta_s, eps, x_scale, xq, nullptr, nullptr}, true);
 }
