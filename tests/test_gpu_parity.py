@@ -55,6 +55,7 @@ RAGGED = [
     (40, 64, 640, "f32", "f32", "per_token", True, 0.6),
     (5, 96, 24576, "bf16", "bf16", "per_token", False, 0.5),
     (6, 64, 49152, "bf16", "bf16", "per_token", False, 0.5),
+    (7, 96, 36928, "bf16", "bf16", "per_token", False, 0.5),   # 4616 chunks: ragged long rows
     (3, 64, 16384 + 64, "bf16", "bf16", "per_token", True, 0.5),
     (4, 40, 133120, "bf16", "bf16", "per_token", False, 0.5),
     # short-K kernel (whole K in LDS): K = 64, 128, 256 with ragged M and N
