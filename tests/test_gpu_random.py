@@ -1,9 +1,10 @@
 """Seeded randomized shapes through the whole path (calibrate, quantize, int8
 GEMM), every element against the oracle: sizes drawn across every kernel's
 range (decode M <= 64, short K of 64 / 128 / 256, the ping-pong tiles, K not a
-multiple of 128, ragged M and N down to 1), with random input dtypes, step
-granularities, weight modes, LayerNorm fold and alpha.  The case list is fixed
-by its seed, so a failure names a reproducible case.
+multiple of 128, ragged M and N down to 1, rows up to 49152 elements), with
+random input dtypes, step granularities, weight modes, LayerNorm fold and
+alpha.  The case lists are fixed by their seeds, so a failure names a
+reproducible case.
 """
 import numpy as np
 import pytest
@@ -35,6 +36,30 @@ def _cases(n=24, seed=20261203):
 
 
 CASES = _cases()
+
+# long rows: every kernel range of the quantizers and the weight path (one-row,
+# two-row, recomputing and per-tensor streaming kernels), smaller M and N
+_KS_LONG = [2048, 2112, 4160, 6144, 8256, 12288, 16384, 16448, 24576, 36928, 49152]
+
+
+def _cases_long(n=40, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        K = int(rng.choice(_KS_LONG))
+        M = int(rng.integers(1, 48))
+        N = int(rng.integers(1, 260))
+        xdt = str(rng.choice(["bf16", "bf16", "f32"]))
+        wdt = str(rng.choice(["bf16", "bf16", "f32"]))
+        mode = str(rng.choice(["per_token", "static", "dynamic_per_tensor"]))
+        wmode = str(rng.choice(["per_channel", "per_tensor"]))
+        ln = bool(rng.random() < 0.3) and K <= 16448
+        alpha = float(rng.choice(datagen.ALPHA_SWEEP))
+        out.append((100 + i, M, N, K, xdt, wdt, mode, wmode, ln, alpha))
+    return out
+
+
+CASES += _cases_long()
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"r{c[0]}_{c[1]}x{c[2]}x{c[3]}_{c[4]}_{c[5]}_"
