@@ -208,10 +208,13 @@ hipError_t run_quantile(const T* x, int64_t rows, int64_t K, int64_t rank0, floa
 // ---- alpha search -----------------------------------------------------------
 
 // Y[m, n] = sum_k X[m, k] W[n, k] in fp64 (the inputs' products are exact in
-// fp64).  128 x 128 output tile per block, 8 x 8 outputs per thread (rows ty +
-// 16 i, columns tx + 16 j), K in steps of 16 staged in LDS: each step's rows
-// arrive as 16-byte loads (8 bf16 or 4 fp32 per lane), all issued before any
-// is converted.  Each output accumulates in increasing k, one fma per k.
+// fp64).  128 x 128 output tile per block, four waves of 64 x 64, each a 4 x 4
+// grid of 16 x 16 v_mfma_f64_16x16x4f64 tiles; K in steps of 16 staged in LDS:
+// each step's rows arrive as 16-byte loads (8 bf16 or 4 fp32 per lane), all
+// issued before any is converted.  The matrix instruction adds its four
+// products to the accumulator in increasing k, so each output is the same as
+// one fma per k in increasing k (measured bit-identical to that loop on the
+// MI355X, and 1.3x faster: 512 x 12288 x 4096 in 1.07 ms instead of 1.39).
 constexpr int kRT = 128;
 constexpr int kRK = 16;
 
@@ -262,22 +265,27 @@ struct RefStage {
     }
 };
 
+typedef double ref_v4d __attribute__((ext_vector_type(4)));
+
 template <typename TX, typename TW>
 __global__ __launch_bounds__(256) void ref_gemm_f64_kernel(const TX* __restrict__ x,
                                                            const TW* __restrict__ w, int64_t M,
                                                            int64_t N, int64_t K,
                                                            double* __restrict__ y) {
-    constexpr int R = kRT / 16;
     __shared__ double As[kRK][kRT + 1];
     __shared__ double Bs[kRK][kRT + 1];
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;  // the wave's 64 x 64 quadrant
     const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRT;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRT;
-    double acc[R][R];
+    // operands: lane l holds A[i = l % 16][k = l / 16] and B[k = l / 16][j = l % 16];
+    // result: lane l holds C[i = l / 16 + 4 r][j = l % 16] in element r
+    const int fi = lane & 15, fk = lane >> 4;
+    ref_v4d acc[4][4];
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < R; ++j) acc[i][j] = 0.0;
+        for (int j = 0; j < 4; ++j) acc[i][j] = ref_v4d{0.0, 0.0, 0.0, 0.0};
     RefStage<TX> sa;
     RefStage<TW> sb;
     for (int64_t k0 = 0; k0 < K; k0 += kRK) {
@@ -287,26 +295,30 @@ __global__ __launch_bounds__(256) void ref_gemm_f64_kernel(const TX* __restrict_
         sb.store(Bs);
         __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < kRK; ++kk) {
-            double a[R], b[R];
+        for (int ks = 0; ks < kRK / 4; ++ks) {
+            double a[4], b[4];
 #pragma unroll
-            for (int i = 0; i < R; ++i) a[i] = As[kk][ty + 16 * i];
+            for (int i = 0; i < 4; ++i) a[i] = As[4 * ks + fk][wm * 64 + i * 16 + fi];
 #pragma unroll
-            for (int j = 0; j < R; ++j) b[j] = Bs[kk][tx + 16 * j];
+            for (int j = 0; j < 4; ++j) b[j] = Bs[4 * ks + fk][wn * 64 + j * 16 + fi];
 #pragma unroll
-            for (int i = 0; i < R; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < R; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const int64_t m = m0 + ty + 16 * i, n = n0 + tx + 16 * j;
-            if (m < M && n < N) y[m * N + n] = acc[i][j];
-        }
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm * 64 + i * 16 + fk + 4 * r;
+                const int64_t n = n0 + wn * 64 + j * 16 + fi;
+                if (m < M && n < N) y[m * N + n] = acc[i][j][r];
+            }
 }
 
 constexpr int kEBlocks = 1024;   // partial sums per reduction
