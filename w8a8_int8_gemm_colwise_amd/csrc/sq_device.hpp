@@ -161,15 +161,6 @@ __device__ __forceinline__ uint2 pack8_bits(const uint32_t (&b)[kChunk]) {
                       __builtin_amdgcn_perm(p67, p45, 0x05040100u));
 }
 
-// Pack 8 codes into two 32-bit words (byte i = element i).
-__device__ __forceinline__ uint2 pack8(const int (&c)[kChunk]) {
-    uint32_t lo = (c[0] & 0xff) | ((c[1] & 0xff) << 8) | ((c[2] & 0xff) << 16) |
-                  (static_cast<uint32_t>(c[3]) << 24);
-    uint32_t hi = (c[4] & 0xff) | ((c[5] & 0xff) << 8) | ((c[6] & 0xff) << 16) |
-                  (static_cast<uint32_t>(c[7]) << 24);
-    return make_uint2(lo, hi);
-}
-
 // Wave-wide (64 lanes) maximum, result valid in every lane.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
