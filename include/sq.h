@@ -163,9 +163,10 @@ sq_status sq_calibrate(const void* x_cal, sq_dtype x_dt, int64_t T,
  *             required for every M); static_scale is not read.
  *   xq [M, K] int8 output codes.
  * Per-token and static: one kernel that reads X once and writes xq (and
- * x_scale) once.  Dynamic per-tensor: a row-maximum pass (the maxima are
- * staged in xq), a one-block reduction into x_scale[0], then the static
- * quantizer with that step -- X is read twice.
+ * x_scale) once.  Dynamic per-tensor: a maximum pass (row maxima, or block
+ * maxima for plain rows of 2048 elements or more, staged in xq), a one-block
+ * reduction into x_scale[0], then the static quantizer with that step -- X is
+ * read twice.
  */
 sq_status sq_smooth_quantize_act(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
                                  const float* s, const float* ln_gamma_s,
