@@ -838,6 +838,7 @@ def main():
                   file=sys.stderr)
             sys.exit(1)
         del ref
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
             graph.replay()
