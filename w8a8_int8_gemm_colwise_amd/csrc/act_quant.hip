@@ -25,7 +25,10 @@
 // saturation count, no codes written).
 // act_quant_multi_kernel (plain) and act_quant_ln2_kernel (LayerNorm) take two
 // bf16 rows per block; act_quant_static_stream_kernel maps long rows
-// elementwise when the step is per tensor.  Same arithmetic per element.
+// elementwise when the step is per tensor; act_quant_long_kernel holds one
+// long plain row per block for the per-token step, with the row's factors
+// requested at the row's start and the next row's chunks during the codes.
+// Same arithmetic per element.
 #include <algorithm>
 
 #include "sq_device.hpp"
@@ -332,6 +335,157 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
             for (int i = 0; i < CPT; ++i) ring[j][i] = ring[j + 1][i];
     }
     if (STATIC && clip) flush_clips(nclip, clip);
+}
+
+// Per-token codes of long plain rows (2048 < chunks <= 6144 with 1024 lanes):
+// one row per block in registers, CPT chunks per lane.  The lane's factors
+// s_k are requested at the start of each row (L2 hits, one round trip per
+// row), the row's own chunks having been requested while the previous row
+// was quantized; each chunk is unpacked and divided once its data are in (a
+// scheduling barrier per chunk keeps the compiler from holding every
+// factor and reciprocal at once), one barrier forms the row maximum, and
+// the next row's chunks are requested before this row's codes are formed
+// and stored.  Whether every factor lies in [2^-126, 2^126), where
+// RN(1/s_k) takes the two-fma sequence of rcp_rn, is decided once per block
+// (FAST); otherwise the IEEE division forms it.  Addresses are uniform bases
+// plus 32-bit byte offsets (rows and s stay far below 4 GiB: K <= SQ_MAX_K).
+// Per element the arithmetic is that of act_quant_kernel.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) char g_cchar;
+typedef const __attribute__((address_space(1))) u32x4_t g_cu32x4;
+typedef __attribute__((address_space(1))) u32x2_t g_u32x2;
+
+__device__ __forceinline__ uint4 gload16(g_cchar* p) {
+    const u32x4_t v = *(g_cu32x4*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <typename T>
+__device__ __forceinline__ RawChunk<T> gload_raw(g_cchar* row, uint32_t c);
+template <>
+__device__ __forceinline__ RawChunk<uint16_t> gload_raw<uint16_t>(g_cchar* row, uint32_t c) {
+    return RawChunk<uint16_t>{gload16(row + c * 16u)};
+}
+template <>
+__device__ __forceinline__ RawChunk<float> gload_raw<float>(g_cchar* row, uint32_t c) {
+    return RawChunk<float>{gload16(row + c * 32u), gload16(row + c * 32u + 16u)};
+}
+
+template <typename T, int CPT, int SP, bool FAST>
+__device__ __forceinline__ void long_rows(const T* __restrict__ x, int64_t M, int64_t K,
+                                          const float* __restrict__ s, int8_t* __restrict__ xq,
+                                          float* __restrict__ x_scale, float* red) {
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int chunks = static_cast<int>(K / kChunk);
+    const int64_t G = gridDim.x;
+    uint32_t off[CPT];  // the lane's chunk indices, clamped into the row
+    bool ok[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * nthr;
+        ok[i] = c < chunks;
+        off[i] = static_cast<uint32_t>(min(c, chunks - 1));
+    }
+    RawChunk<T> ring[CPT];
+    int64_t m = blockIdx.x;
+    if (m < M) {
+        g_cchar* xr = (g_cchar*)(x + m * K);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) ring[i] = gload_raw<T>(xr, off[i]);
+    }
+    int parity = 0;
+    for (; m < M; m += G, parity ^= 1) {
+        // an opaque factor base and opaque copies of the offsets keep the
+        // loads and their address arithmetic in the loop (hoisted, 64-bit
+        // addresses would hold registers for the whole row)
+        g_cchar* sb = (g_cchar*)s;
+        asm volatile("" : "+s"(sb));
+        uint32_t o[CPT];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            o[i] = off[i];
+            asm volatile("" : "+v"(o[i]));
+        }
+        // factors of SP chunks in flight: chunk i's turn requests chunk i + SP
+        float sf[CPT][kChunk];
+        auto load_sf = [&](int i) {
+            const uint4 a = gload16(sb + o[i] * 32u), b = gload16(sb + o[i] * 32u + 16u);
+            sf[i][0] = __uint_as_float(a.x); sf[i][1] = __uint_as_float(a.y);
+            sf[i][2] = __uint_as_float(a.z); sf[i][3] = __uint_as_float(a.w);
+            sf[i][4] = __uint_as_float(b.x); sf[i][5] = __uint_as_float(b.y);
+            sf[i][6] = __uint_as_float(b.z); sf[i][7] = __uint_as_float(b.w);
+        };
+#pragma unroll
+        for (int i = 0; i < SP; ++i) load_sf(i);
+        __builtin_amdgcn_sched_barrier(0);
+        float v[CPT][kChunk];
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            // no branch on ok[i]: a lane past the row's end holds a copy of the
+            // row's last chunk, which leaves the row maximum unchanged, and
+            // every lane then passes the same waits
+            if (i + SP < CPT) load_sf(i + SP);
+            unpack(ring[i], v[i]);
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                const float b = sf[i][e];
+                float rb;
+                if constexpr (FAST) {
+                    const float r = __builtin_amdgcn_rcpf(b);
+                    rb = __builtin_fmaf(__builtin_fmaf(-b, r, 1.0f), r, r);
+                } else {
+                    rb = 1.0f / b;
+                }
+                v[i][e] = div_x<T>(v[i][e], b, rb);
+                mx = fmaxf(mx, fabsf(v[i][e]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mx = block_max(mx, red, parity);
+        const float d = step_from_absmax(mx);
+        const float rd = 1.0f / d;
+        if (tid == 0) x_scale[m] = d;
+        if (m + G < M) {
+            g_cchar* xr = (g_cchar*)(x + (m + G) * K);
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) ring[i] = gload_raw<T>(xr, o[i]);
+        }
+        __attribute__((address_space(1))) char* orow =
+            (__attribute__((address_space(1))) char*)(xq + m * K);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            uint32_t q[kChunk];
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) q[e] = quantize<false>(v[i][e], d, rd);
+            const uint2 packed = pack8_bits(q);
+            if (ok[i]) *(g_u32x2*)(orow + o[i] * 8u) = u32x2_t{packed.x, packed.y};
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+template <typename T, int CPT>
+__global__ __launch_bounds__(1024) void act_quant_long_kernel(
+    const T* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ s,
+    int8_t* __restrict__ xq, float* __restrict__ x_scale) {
+    __shared__ float red[32];
+    const int64_t chunks = K / kChunk;
+    int in_range = 1;
+    for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
+        float sv[kChunk];
+        load_chunk(s, c, sv);
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e)
+            in_range &= (sv[e] >= 0x1p-126f && sv[e] < 0x1p126f) ? 1 : 0;
+    }
+    constexpr int SP = CPT < 3 ? CPT : 3;
+    if (__syncthreads_and(in_range))
+        long_rows<T, CPT, SP, true>(x, M, K, s, xq, x_scale, red);
+    else
+        long_rows<T, CPT, SP, false>(x, M, K, s, xq, x_scale, red);
 }
 
 // R rows at once (plain mode, codes of the per-token or static quantizer):
@@ -985,6 +1139,29 @@ hipError_t run_static_stream(const ActArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Per-token codes of rows of 2049-6144 chunks: four chunks per lane up to
+// 4096 chunks, six beyond, at most 1024 lanes, one block per CU.  Measured on
+// the MI355X against act_quant_kernel (eight chunks per lane, factors loaded
+// chunk by chunk after the row had landed), codes and steps identical, caches
+// flushed before each call: 4096 x 49152 bf16 140-145 us vs 192-198 (4.2-4.3
+// TB/s), 4096 x 36864 110-115 vs 154-160, 4096 x 24576 75-81 vs 90-93,
+// 2048 x 32768 56-58 vs 62-64, 4096 x 16448 64-66 vs 74-76.  Requesting the
+// next row's first factors before this row's stores (so that the first wait
+// of a row does not also wait for them) was no faster.
+template <typename T>
+hipError_t run_long(const ActArgs& a, hipStream_t stream) {
+    const int64_t chunks = a.K / kChunk;
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.M, 256));
+    if (chunks <= 4 * 1024) {
+        act_quant_long_kernel<T, 4><<<grid, round_up64((chunks + 3) / 4), 0, stream>>>(
+            static_cast<const T*>(a.x), a.M, a.K, a.s, a.xq, a.x_scale);
+    } else {
+        act_quant_long_kernel<T, 6><<<grid, round_up64((chunks + 5) / 6), 0, stream>>>(
+            static_cast<const T*>(a.x), a.M, a.K, a.s, a.xq, a.x_scale);
+    }
+    return hipGetLastError();
+}
+
 template <typename T, bool STATIC>
 hipError_t dispatch_plain(const ActArgs& a, hipStream_t stream) {
     const int64_t chunks = a.K / kChunk;
@@ -999,11 +1176,14 @@ hipError_t dispatch_plain(const ActArgs& a, hipStream_t stream) {
     if (chunks <= 32) return run_rows<T, STATIC, 32>(a, stream);
     // rows up to 2048 chunks: one or two 16-byte loads per lane and row with the
     // per-column constants cached and the next row prefetched (measured: one
-    // prefetched row beats deeper rings on the MI355X); longer rows:
-    // four (up to 1024 lanes) or eight (up to 768 lanes) loads per lane without
-    // caching; past that the multi-sweep kernel
+    // prefetched row beats deeper rings on the MI355X); longer rows: per-token
+    // codes in act_quant_long_kernel, the count and row-maximum passes with
+    // four (up to 1024 lanes) or eight (up to 768 lanes) loads per lane
+    // without caching; past that the multi-sweep kernel
     if (chunks <= 64) return run<T, false, STATIC, 1, 1>(a, 64, stream);
     if (chunks <= 2048) return run<T, false, STATIC, 2, 1>(a, round_up64((chunks + 1) / 2), stream);
+    if (!STATIC && a.rowmax == nullptr && a.clip == nullptr && chunks <= 6 * 1024)
+        return run_long<T>(a, stream);
     if (chunks <= 4 * 1024) return run<T, false, STATIC, 4, 0>(a, round_up64((chunks + 3) / 4), stream);
     if (chunks <= 8 * 768)
         return run<T, false, STATIC, 8, 0, 768>(a, round_up64((chunks + 7) / 8), stream);
