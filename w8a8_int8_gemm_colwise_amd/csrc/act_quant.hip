@@ -517,17 +517,34 @@ __global__ __launch_bounds__(NT) void act_quant_multi_kernel(
         }
     };
     int64_t m0 = static_cast<int64_t>(blockIdx.x) * R;
-    fetch(m0);
+    // the factors are requested before the first rows, so that their
+    // reciprocals are formed while the rows are still in flight (loads
+    // complete in order: requested after the rows, the factors would wait for
+    // them); lanes past the row's end read its last chunk and use nothing.
+    // Measured on the MI355X against the rows-first order, outputs identical,
+    // caches flushed before each call: 2048 x 4096 11.5-11.7 us vs 12.4-12.7,
+    // 2048 x 16384 24.8-25.2 vs 25.4-26.2, 4096 x 12288 34.9-35.8 vs 35.0-36.4
     float c0[CPT][kChunk], c1[CPT][kChunk];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int64_t c = tid + static_cast<int64_t>(i) * NT;
-        if (c < chunks) {
-            load_chunk(s, c, c0[i]);
+    for (int i = 0; i < CPT; ++i)
+        load_chunk(s, min(tid + static_cast<int64_t>(i) * NT, chunks - 1), c0[i]);
+    __builtin_amdgcn_sched_barrier(0);
+    // the block's first rows, without a branch per load (a skipped load would
+    // make the compiler wait for every load before the first reciprocal): a
+    // row past the batch (odd M) reads the last row and is never stored, a
+    // chunk past the row's end reads its last chunk and is never used
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) c1[i][e] = rcp_rn(c0[i][e]);
-        }
+    for (int r = 0; r < R; ++r) {
+        const int64_t m = min(m0 + r, M - 1);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+            raw[r][i] = load_raw(x + m * K, min(tid + static_cast<int64_t>(i) * NT, chunks - 1));
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) c1[i][e] = rcp_rn(c0[i][e]);
     float d_static = 0.0f, rd_static = 0.0f;
     if (STATIC) {
         d_static = *static_scale;
