@@ -350,17 +350,6 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
 // (FAST); otherwise the IEEE division forms it.  Addresses are uniform bases
 // plus 32-bit byte offsets (rows and s stay far below 4 GiB: K <= SQ_MAX_K).
 // Per element the arithmetic is that of act_quant_kernel.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef const __attribute__((address_space(1))) char g_cchar;
-typedef const __attribute__((address_space(1))) u32x4_t g_cu32x4;
-typedef __attribute__((address_space(1))) u32x2_t g_u32x2;
-
-__device__ __forceinline__ uint4 gload16(g_cchar* p) {
-    const u32x4_t v = *(g_cu32x4*)p;
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 template <typename T>
 __device__ __forceinline__ RawChunk<T> gload_raw(g_cchar* row, uint32_t c);
 template <>
@@ -410,13 +399,7 @@ __device__ __forceinline__ void long_rows(const T* __restrict__ x, int64_t M, in
         }
         // factors of SP chunks in flight: chunk i's turn requests chunk i + SP
         float sf[CPT][kChunk];
-        auto load_sf = [&](int i) {
-            const uint4 a = gload16(sb + o[i] * 32u), b = gload16(sb + o[i] * 32u + 16u);
-            sf[i][0] = __uint_as_float(a.x); sf[i][1] = __uint_as_float(a.y);
-            sf[i][2] = __uint_as_float(a.z); sf[i][3] = __uint_as_float(a.w);
-            sf[i][4] = __uint_as_float(b.x); sf[i][5] = __uint_as_float(b.y);
-            sf[i][6] = __uint_as_float(b.z); sf[i][7] = __uint_as_float(b.w);
-        };
+        auto load_sf = [&](int i) { gload8f(sb + o[i] * 32u, sf[i]); };
 #pragma unroll
         for (int i = 0; i < SP; ++i) load_sf(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -453,15 +436,14 @@ __device__ __forceinline__ void long_rows(const T* __restrict__ x, int64_t M, in
 #pragma unroll
             for (int i = 0; i < CPT; ++i) ring[i] = gload_raw<T>(xr, o[i]);
         }
-        __attribute__((address_space(1))) char* orow =
-            (__attribute__((address_space(1))) char*)(xq + m * K);
+        g_char* orow = (g_char*)(xq + m * K);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             uint32_t q[kChunk];
 #pragma unroll
             for (int e = 0; e < kChunk; ++e) q[e] = quantize<false>(v[i][e], d, rd);
             const uint2 packed = pack8_bits(q);
-            if (ok[i]) *(g_u32x2*)(orow + o[i] * 8u) = u32x2_t{packed.x, packed.y};
+            if (ok[i]) gstore8(orow + o[i] * 8u, packed);
             __builtin_amdgcn_sched_barrier(0);
         }
     }

@@ -493,10 +493,13 @@ __global__ __launch_bounds__(256) void weight_quant_stream_kernel(
 
 // Per-channel step, bf16 rows of 4097-6144 chunks: the packed row stays in
 // registers and RN(w s) is formed twice (for the row maximum, then for the
-// codes) with s read from L2 both times, so only the packed row is held and two
-// blocks fit on a CU.  Measured on the MI355X against the one-row kernel with
-// the products held (12288 x 49152): 438 vs 534 us with flushed caches, 412 vs
-// 502 us warm; identical codes and steps.
+// codes) with s read from L2 both times, so only the packed row is held (115
+// VGPRs, one block of 1024 lanes per CU).  Measured on the MI355X against the
+// one-row kernel with the products held (12288 x 49152): 438 vs 534 us with
+// flushed caches, 412 vs 502 us warm; identical codes and steps.  A form with
+// the factors requested two chunks ahead, 32-bit offsets and every load and
+// store issued was slower (12288 x 49152 431-455 us vs 380-402, 12288 x
+// 36864 365-400 vs 287-302).
 template <int CPT, int NT>
 __global__ __launch_bounds__(NT, 2) void weight_quant_recompute_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,

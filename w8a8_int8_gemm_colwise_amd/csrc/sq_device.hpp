@@ -59,6 +59,35 @@ __device__ __forceinline__ RawChunk<float> load_raw<float>(const float* row, int
     return RawChunk<float>{p[0], p[1]};
 }
 
+// Global-memory access through a uniform base plus a 32-bit byte offset (the
+// scalar-base load form, one offset register per access; every row and
+// vector here lies far below 4 GiB).  Vector types are plain ext_vector
+// types: HIP's vector classes cannot be copied out of address space 1.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) char g_cchar;
+typedef __attribute__((address_space(1))) char g_char;
+typedef const __attribute__((address_space(1))) u32x4_t g_cu32x4;
+typedef __attribute__((address_space(1))) u32x2_t g_u32x2;
+
+__device__ __forceinline__ uint4 gload16(g_cchar* p) {
+    const u32x4_t v = *(g_cu32x4*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Eight fp32 values (32 bytes) at p.
+__device__ __forceinline__ void gload8f(g_cchar* p, float (&v)[kChunk]) {
+    const uint4 a = gload16(p), b = gload16(p + 16);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+
+__device__ __forceinline__ void gstore8(g_char* p, uint2 v) {
+    *(g_u32x2*)p = u32x2_t{v.x, v.y};
+}
+
 __device__ __forceinline__ void unpack(const RawChunk<uint16_t>& r, float* v) {
     v[0] = bf16_lo(r.u.x); v[1] = bf16_hi(r.u.x);
     v[2] = bf16_lo(r.u.y); v[3] = bf16_hi(r.u.y);
