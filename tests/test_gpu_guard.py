@@ -8,8 +8,9 @@ oracle).  Shapes are ragged in M and N (rows of odd byte length, partial
 tiles) and pick every GEMM kernel -- ping-pong 256x128, 256x256 and the mixed
 launch, short K, the decode kernel and both register-staged fallbacks, plus the
 batched product -- every activation-quantizer kernel (short rows packed in a
-wave, cached and uncached rows, the multi-sweep kernel, LayerNorm variants;
-per-token, static and dynamic per-tensor), the calibration kernels (weight
+wave, cached and uncached rows, the long-row kernel with lanes past the
+row's end, the multi-sweep kernel, LayerNorm variants; per-token, static and
+dynamic per-tensor), the calibration kernels (weight
 rows of every length, per channel and per tensor, with and without the
 LayerNorm fold) and the robust-calibration calls.
 """
@@ -125,7 +126,7 @@ def test_batched_outputs_stay_in_bounds(K):
         same(f"y[{out}]", g.t, ref)
 
 
-ACT_K = [64, 128, 256, 512, 4096, 16384, 24576, 49152, 65536]
+ACT_K = [64, 128, 256, 512, 4096, 16384, 16448, 24576, 32832, 49152, 65536]
 
 
 @pytest.mark.parametrize("K", ACT_K)
