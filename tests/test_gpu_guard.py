@@ -153,7 +153,7 @@ def test_activation_quantizer_stays_in_bounds(K, mode):
         same("x_scale", gs.t, ref_s)
 
 
-@pytest.mark.parametrize("K", [512, 4096, 8192, 16384, 24576])
+@pytest.mark.parametrize("K", [512, 4096, 8192, 10240, 14400, 16384, 24576])
 @pytest.mark.parametrize("mode", ["per_token", "static", "dynamic_per_tensor"])
 def test_layernorm_quantizer_stays_in_bounds(K, mode):
     d = dev()

@@ -1,8 +1,9 @@
 """LayerNorm-mode activation quantizer against the oracle, every element: row
-lengths on both sides of each kernel boundary of the LayerNorm dispatch (one,
-two, three and four 16-byte chunks per lane of 256, ragged chunk counts, and
-the first length past the two-row kernel), token counts that leave a partial
-last sweep of the grid and an odd last row pair, and the three step modes.
+lengths on both sides of each kernel boundary of the LayerNorm dispatch (one
+to four 16-byte chunks per lane of 256 in the two-row kernel, five to eight in
+the wide-row kernel, ragged chunk counts), token counts that leave a partial
+last sweep of the grid and an odd last row pair, fp32 inputs, and the three
+step modes.
 Codes, per-token steps and the batch step must match bit for bit.
 """
 import numpy as np
@@ -26,8 +27,13 @@ CASES = [
     (7, 4160, "bf16"),      # 520 chunks: three per lane
     (130, 6144, "bf16"),
     (2051, 8192, "bf16"),   # four per lane, two sweeps and a ragged tail
-    (33, 8256, "bf16"),     # 1032 chunks: the one-row kernel
+    (33, 8256, "bf16"),     # 1032 chunks: the wide-row kernel, six chunks per lane
+    (1100, 10240, "bf16"),  # 1280 chunks, five of six per lane; tokens past one sweep of 1024 blocks
+    (5, 12288, "bf16"),     # 1536 chunks: six per lane
+    (801, 14400, "bf16"),   # 1800 chunks: eight per lane, ragged; tokens past one sweep of 768 blocks
+    (9, 16384, "bf16"),     # 2048 chunks: eight per lane
     (65, 4096, "f32"),      # fp32 input: the one-row kernel
+    (7, 12288, "f32"),      # fp32 input past 1024 chunks: the one-row kernel
 ]
 MODES = ["per_token", "static", "dynamic_per_tensor"]
 

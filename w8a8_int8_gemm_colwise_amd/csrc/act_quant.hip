@@ -27,8 +27,9 @@
 // bf16 rows per block; act_quant_static_stream_kernel maps long rows
 // elementwise when the step is per tensor; act_quant_long_kernel holds one
 // long plain row per block for the per-token step, with the row's factors
-// requested at the row's start and the next row's chunks during the codes.
-// Same arithmetic per element.
+// requested at the row's start and the next row's chunks during the codes;
+// act_quant_ln_row_kernel is the LayerNorm-mode codes kernel for rows of
+// 1025-2048 chunks.  Same arithmetic per element.
 #include <algorithm>
 
 #include "sq_device.hpp"
@@ -856,6 +857,122 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_ln2_kernel(
     }
 }
 
+// LayerNorm mode, codes of bf16 rows of 1025-2048 chunks (K 8200-16384).
+// Measured on the MI355X against act_quant_kernel in LayerNorm mode, codes and
+// steps identical, caches flushed before each call: 4096 x 9216 38.7-39.4 us
+// vs 47.7-49.1, 4096 x 12288 44.7-46.3 vs 53.8-55.7, 4096 x 16384 58.3-60.4 vs
+// 63.7-67.8; a form with four rows per 1024-lane block and the factors staged
+// in LDS was slower than either (4096 x 12288 81 us).  One row per block of
+// exactly 256 lanes (lane t owns canonical partial t: chunks
+// t + 256 i, increasing k within the partial, then the fixed halving tree), as
+// in act_quant_kernel, without its count and row-maximum passes.  Every load
+// is issued (clamped indices; a chunk past the row's end is never used), so
+// the compiler's waits count exactly; gamma'_k and beta'_k of the first SP
+// chunks are requested before the mean reduction and each chunk's turn
+// requests those SP chunks ahead, instead of one L2 round trip per chunk after
+// the variance; a scheduling barrier per chunk bounds the registers held.
+template <bool STATIC, int CPT, int SP>
+__global__ __launch_bounds__(kLnThreads) void act_quant_ln_row_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ gs,
+    const float* __restrict__ bs, float eps, const float* __restrict__ static_scale,
+    int8_t* __restrict__ xq, float* __restrict__ x_scale) {
+    __shared__ float lds[2 * kLnThreads + 32];
+    const int t = threadIdx.x;
+    const int chunks = static_cast<int>(K / kChunk);
+    const float kf = static_cast<float>(K);
+    float d_static = 0.0f, rd_static = 0.0f;
+    if (STATIC) {
+        d_static = *static_scale;
+        rd_static = 1.0f / d_static;
+    }
+    int parity = 0;
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x, parity ^= 1) {
+        // uniform bases plus 32-bit offsets (K <= SQ_MAX_K), formed in the row
+        // loop from opaque copies: the compiler neither hoists the factor loads
+        // to the top of the row nor holds 64-bit addresses across it
+        g_cchar* gb = (g_cchar*)gs;
+        g_cchar* bb = (g_cchar*)bs;
+        asm volatile("" : "+s"(gb), "+s"(bb));
+        uint32_t o[CPT];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            o[i] = static_cast<uint32_t>(min(t + i * kLnThreads, chunks - 1));
+            asm volatile("" : "+v"(o[i]));
+        }
+        g_cchar* xr = (g_cchar*)(x + m * K);
+        RawChunk<uint16_t> raw[CPT];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) raw[i] = RawChunk<uint16_t>{gload16(xr + o[i] * 16u)};
+        float ga[CPT][kChunk], be[CPT][kChunk];
+#pragma unroll
+        for (int i = 0; i < SP; ++i) {
+            gload8f(gb + o[i] * 32u, ga[i]);
+            gload8f(bb + o[i] * 32u, be[i]);
+        }
+        float v[CPT][kChunk];
+        float p = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            unpack(raw[i], v[i]);
+            if (t + i * kLnThreads < chunks) {
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) p = p + v[i][e];
+            }
+        }
+        const float mu = canonical_tree(p, lds) / kf;
+        p = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            if (t + i * kLnThreads < chunks) {
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) {
+                    v[i][e] = v[i][e] - mu;
+                    const float dd = v[i][e] * v[i][e];
+                    p = p + dd;
+                }
+            }
+        }
+        const float var = canonical_tree(p, lds + kLnThreads) / kf;
+        const float rho = 1.0f / __builtin_sqrtf(var + eps);
+        asm volatile("" : "+s"(gb), "+s"(bb));
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            if (i + SP < CPT) {
+                gload8f(gb + o[i + SP] * 32u, ga[i + SP]);
+                gload8f(bb + o[i + SP] * 32u, be[i + SP]);
+            }
+            if (t + i * kLnThreads < chunks) {
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) {
+                    float q = v[i][e] * rho;
+                    q = q * ga[i][e];
+                    v[i][e] = q + be[i][e];
+                    mx = fmaxf(mx, fabsf(v[i][e]));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float d = d_static, rd = rd_static;
+        if (!STATIC) {
+            mx = block_max(mx, lds + 2 * kLnThreads, parity);
+            d = step_from_absmax(mx);
+            rd = 1.0f / d;
+            if (t == 0) x_scale[m] = d;
+        }
+        g_char* orow = (g_char*)(xq + m * K);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            uint32_t q[kChunk];
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[i][e], d, rd);
+            const uint2 packed = pack8_bits(q);
+            if (t + i * kLnThreads < chunks) gstore8(orow + o[i] * 8u, packed);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // Short rows (plain mode, K <= 256: at most 32 chunks).  A wave quantizes
 // 64 / SG rows at once, SG lanes per row (SG = the chunk count rounded up to a
 // power of two): lane l owns chunk l % SG of row l / SG, so its s_k and
@@ -1219,12 +1336,30 @@ hipError_t run_ln2(const ActArgs& a, int64_t need, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// LayerNorm mode, codes of bf16 rows of 1025-2048 chunks: one row per block of
+// 256 lanes, six or eight chunks per lane; the grid is the blocks that fit at
+// once (126 VGPRs at six chunks per lane: four per CU; 146 at eight: three).
+template <bool STATIC>
+hipError_t run_ln_row(const ActArgs& a, int64_t need, hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.M, need <= 6 ? 1024 : 768));
+    const uint16_t* x = static_cast<const uint16_t*>(a.x);
+    if (need <= 6)
+        act_quant_ln_row_kernel<STATIC, 6, 2><<<grid, kLnThreads, 0, stream>>>(
+            x, a.M, a.K, a.gs, a.bs, a.eps, a.static_scale, a.xq, a.x_scale);
+    else
+        act_quant_ln_row_kernel<STATIC, 8, 2><<<grid, kLnThreads, 0, stream>>>(
+            x, a.M, a.K, a.gs, a.bs, a.eps, a.static_scale, a.xq, a.x_scale);
+    return hipGetLastError();
+}
+
 template <typename T, bool STATIC>
 hipError_t dispatch_ln(const ActArgs& a, hipStream_t stream) {
     const int64_t chunks = a.K / kChunk;
     const int64_t need = (chunks + kLnThreads - 1) / kLnThreads;
     if (sizeof(T) == 2 && a.rowmax == nullptr && a.clip == nullptr && need <= 4)
         return run_ln2<STATIC>(a, need, stream);
+    if (sizeof(T) == 2 && a.rowmax == nullptr && a.clip == nullptr && need <= 8)
+        return run_ln_row<STATIC>(a, need, stream);
     if (need <= 1) return run<T, true, STATIC, 1, 1, kLnThreads>(a, kLnThreads, stream);
     if (need <= 2) return run<T, true, STATIC, 2, 1, kLnThreads>(a, kLnThreads, stream);
     if (need <= 4) return run<T, true, STATIC, 4, 1, kLnThreads>(a, kLnThreads, stream);
