@@ -170,35 +170,34 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
     constexpr int CC = CACHE ? CPT : 1;
     const int64_t G = gridDim.x;
 
+    // Every row and constant load is issued, so the compiler's waits count the
+    // loads in flight exactly (a load skipped on some path makes it wait for
+    // all of them, the prefetch just issued included): a chunk past the row's
+    // end reads the row's last chunk and every use of it is guarded, and a
+    // prefetch past the batch re-reads the block's current row (an L2 hit).
+    auto lane_chunk = [&](int i) { return min(tid + static_cast<int64_t>(i) * nthr, chunks - 1); };
     RawChunk<T> ring[D + 1][CPT];
     auto fetch = [&](int64_t m, RawChunk<T> (&r)[CPT]) {
         const T* row = x + m * K;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
-            if (c < chunks) r[i] = load_raw(row, c);
-        }
+        for (int i = 0; i < CPT; ++i) r[i] = load_raw(row, lane_chunk(i));
     };
     // the first rows' loads go out before the per-column set-up below
 #pragma unroll
-    for (int j = 0; j < D; ++j)
-        if (blockIdx.x + j * G < M) fetch(blockIdx.x + j * G, ring[j]);
+    for (int j = 0; j < D; ++j) fetch(min(blockIdx.x + j * G, M - 1), ring[j]);
 
     // per-column constants: c0 = s (plain) or gamma' (LN); c1 = 1/s or beta'
     float c0[CC][kChunk], c1[CC][kChunk];
     if (CACHE) {
 #pragma unroll
         for (int i = 0; i < CC; ++i) {
-            const int64_t c = tid + static_cast<int64_t>(i) * nthr;
-            if (c < chunks) {
-                if (LN) {
-                    load_chunk(gs, c, c0[i]);
-                    load_chunk(bs, c, c1[i]);
-                } else {
-                    load_chunk(s, c, c0[i]);
+            if (LN) {
+                load_chunk(gs, lane_chunk(i), c0[i]);
+                load_chunk(bs, lane_chunk(i), c1[i]);
+            } else {
+                load_chunk(s, lane_chunk(i), c0[i]);
 #pragma unroll
-                    for (int e = 0; e < kChunk; ++e) c1[i][e] = rcp_rn(c0[i][e]);
-                }
+                for (int e = 0; e < kChunk; ++e) c1[i][e] = rcp_rn(c0[i][e]);
             }
         }
     }
@@ -210,7 +209,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
     int nclip = 0;
     int parity = 0;
     for (int64_t m = blockIdx.x; m < M; m += G, parity ^= 1) {
-        if (m + D * G < M) fetch(m + D * G, ring[D]);
+        fetch(m + D * G < M ? m + D * G : m, ring[D]);
         float v[CPT][kChunk];
 #pragma unroll
         for (int i = 0; i < CPT; ++i) unpack(ring[0][i], v[i]);
