@@ -160,6 +160,27 @@ __device__ __forceinline__ float step_from_absmax(float m) {
     return fmaxf(m, kFloor) / kQmax;
 }
 
+// The step d = step_from_absmax(m) and rd = RN(1/d) together, equal to the two
+// IEEE divisions.  For finite m the quotient by 127 is div_rn with the
+// correctly rounded constant RN(1/127) (FLOOR/127 > 2^-31, so no residual
+// underflows), and d then lies in [2^-31, 2^121), where rcp_rn's two-fma
+// sequence is exact; an infinite maximum takes the divisions (fmaxf already
+// maps NaN to FLOOR).  About ten VALU operations instead of two division
+// sequences; m is the same in every lane that forms a row's step, so the
+// branch does not diverge.
+__device__ __forceinline__ void step_rcp(float m, float& d, float& rd) {
+    constexpr float kRcpQmax = 1.0f / kQmax;
+    const float a = fmaxf(m, kFloor);
+    if (a < __builtin_inff()) {
+        d = div_rn(a, kQmax, kRcpQmax);
+        const float r = __builtin_amdgcn_rcpf(d);
+        rd = __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+    } else {
+        d = a / kQmax;
+        rd = 1.0f / d;
+    }
+}
+
 // rne then clamp to [-127, 127], as an int.
 __device__ __forceinline__ int code_of(float q) {
     float r = __builtin_rintf(q);
