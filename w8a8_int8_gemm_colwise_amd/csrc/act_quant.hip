@@ -1207,9 +1207,9 @@ hipError_t run_rows(const ActArgs& a, hipStream_t stream) {
 }
 
 // Two rows at once per block (bf16 codes, 64 < chunks <= 2048): one lane per
-// chunk for rows of up to 512 chunks (128, 256 or 512 lanes; at most 1024 blocks
-// of 512 lanes or 2048 smaller ones), else up to 1024 lanes with two chunks each
-// (one block per CU).  Measured on the MI355X against one row per block: 8-12%
+// chunk for rows of up to 512 chunks (128, 256 or 512 lanes; at most 768, 1536
+// or 2048 blocks), else up to 1024 lanes with two chunks each (one block per
+// CU).  Measured on the MI355X against one row per block: 8-12%
 // faster on 2048 x 4096 and 2048 x 16384, within 3% on 65536 x 2048, 5% faster on
 // 8192 x 1024.
 template <bool STATIC>
@@ -1218,7 +1218,13 @@ hipError_t run_multi(const ActArgs& a, hipStream_t stream) {
     const int64_t pairs = (a.M + 1) / 2;
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     if (chunks <= 512) {
-        const unsigned cap = chunks > 256 ? 1024u : 2048u;
+        // at most the blocks one round holds (72 VGPRs: three blocks of 512
+        // lanes or seven of 256 per CU); the rest take further row pairs
+        // with the next pair in flight.  Measured against 1024 / 2048 blocks,
+        // outputs identical, caches flushed: 2048 x 4096 10.7 us vs 11.0,
+        // 4096 x 4096 13.9 vs 14.7-15.0, 2048 x 3072 9.8 vs 10.5, 16384 x 2048
+        // 21.2 vs 23.1 (1536 blocks of 256 lanes)
+        const unsigned cap = chunks > 256 ? 768u : chunks > 128 ? 1536u : 2048u;
         const unsigned grid = static_cast<unsigned>(std::min<int64_t>(pairs, cap));
         if (chunks <= 128)
             act_quant_multi_kernel<uint16_t, STATIC, 1, 2, 128><<<grid, 128, 0, stream>>>(
