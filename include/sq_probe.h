@@ -69,6 +69,19 @@ int sqp_check_div_narrow(int raw, unsigned long long* counts, uint32_t* first_ba
 int sqp_check_div(uint32_t seed, uint32_t count, int raw, unsigned long long* counts,
                   uint32_t* first_bad, sqp_stream_t stream);
 
+/* sqp_check_codes: the quantizers' code step (chunk_codes, eight values at a
+ * time: rne of the correctly rounded quotient by the step, taken from the
+ * exact product with RN(1/step) unless a half-integer lies within its error
+ * bound) on `count` chunks hashed from (seed, key): per chunk a step formed
+ * from a maximum in [2^-30, 2^30) as the kernels form it, values (k + f) times
+ * the step with f uniform or within 4 ulps of 1/2 (ties); clamp != 0 the
+ * static quantizer's form (|k| up to 140, dividends limited to +-128 steps,
+ * codes clamped to +-127).  counts[0] += codes that differ from those of the
+ * compiler's IEEE quotient; counts[1] is unused.  raw != 0: the short form
+ * without its fallback (the negative control).  Key = chunk index. */
+int sqp_check_codes(uint32_t seed, uint32_t count, int clamp, int raw, unsigned long long* counts,
+                    uint32_t* first_bad, sqp_stream_t stream);
+
 /* q[i] = a[i] / b[i] with the compiler's fp32 division (n elements), so the
  * host can confirm that division is the correctly rounded one. */
 int sqp_div_ref(const float* a, const float* b, float* q, int64_t n, sqp_stream_t stream);

@@ -166,7 +166,7 @@ def test_probe_library_exports_and_validates():
     text = open(os.path.join(ROOT, "include", "sq_probe.h")).read()
     names = set(re.findall(r"^\s*int\s+(sqp_\w+)\s*\(", text, flags=re.M))
     assert names == {"sqp_mfma_i8", "sqp_read", "sqp_copy", "sqp_check_rcp",
-                     "sqp_check_div_narrow", "sqp_check_div", "sqp_div_ref"}
+                     "sqp_check_div_narrow", "sqp_check_div", "sqp_check_codes", "sqp_div_ref"}
     out = subprocess.run(["nm", "-D", "--defined-only", probes.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     assert names <= set(re.findall(r" T (sqp_\w+)$", out, flags=re.M))
@@ -183,6 +183,8 @@ def test_probe_library_exports_and_validates():
     assert L.sqp_check_rcp(0x3F800000, 0x7F800001, 0, P, P, None) == 1   # past +inf
     assert L.sqp_check_div_narrow(0, P, None, None) == 1
     assert L.sqp_check_div(1, 0, 0, P, P, None) == 1
+    assert L.sqp_check_codes(1, 0, 0, 0, P, P, None) == 1
+    assert L.sqp_check_codes(1, 4, 1, 0, None, P, None) == 1
     assert L.sqp_div_ref(P, P, P, 0, None) == 1
 
 

@@ -8,6 +8,9 @@ on these sequences returning the correctly rounded quotient:
   div_rn_narrow(a,b,r) three operations, claimed = RN(a/b) when a has at most
                        8 significant bits (bf16 activations)
   div_rn(a,b,r)        five operations, RN(a/b) by Markstein's theorem
+  chunk_codes          the int8 codes rne(RN(v/d)) of eight values from the
+                       exact product v * RN(1/d), deferring to div_rn near
+                       half-integers
 
 The check kernels (libsqprobe.so, compiled from the same device functions)
 decide correct rounding exactly from the fp64 residual a - b q, with no
@@ -52,6 +55,20 @@ def test_div_rn_fp32_dividends():
     assert probes.check_div(d, seed=20251203, count=1 << 30) == (0, 0, None)
     bad, _, _ = probes.check_div(d, seed=20251203, count=1 << 24, raw=True)
     assert bad > 0
+
+
+@pytest.mark.parametrize("clamp", [False, True], ids=["row-step", "static"])
+def test_chunk_codes_match_the_division(clamp):
+    """The quantizers' code step (chunk_codes) takes rne of the exact product
+    with RN(1/step) and defers to the division only where a half-integer lies
+    within that product's error bound; its codes must equal those of the IEEE
+    quotient on 2^27 values, half of them exact ties or within 4 ulps of one."""
+    d = dev()
+    say(f"[case] chunk_codes clamp={clamp}: 2^24 hashed chunks of 8 values")
+    assert probes.check_codes(d, seed=20251204, count=1 << 24, clamp=clamp) == (0, 0, None)
+    bad, _, first = probes.check_codes(d, seed=20251204, count=1 << 20, clamp=clamp, raw=True)
+    say(f"  short form without the fallback: {bad} of 2^23 codes wrong")
+    assert bad > 0 and first is not None
 
 
 def test_compiler_division_is_the_ieee_division():

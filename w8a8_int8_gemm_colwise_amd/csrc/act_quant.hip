@@ -13,8 +13,10 @@
 // chunks of 8 elements (chunk c = tid + i*blockDim), so per-column data
 // (1/s_k, rcp_rn) is computed once per block and reused across the rows the
 // block walks.  The row stays in registers between the absmax reduction and
-// the quantize pass.  Divisions by s_k and by the step use div_rn() (correctly
-// rounded, five VALU ops; three for x / s_k when x is bf16, div_x).  LayerNorm
+// the quantize pass.  Divisions by s_k use div_rn() (correctly rounded, five
+// VALU ops; three when x is bf16, div_x); the codes come from chunk_codes
+// (rne of the correctly rounded quotient by the step, without the division
+// except where a half-integer lies within its error bound).  LayerNorm
 // mode uses exactly 256 lanes so that lane t owns partial t of the canonical
 // fp32 reduction (chunk c -> partial c mod 256, increasing k within a partial,
 // then the fixed halving tree).
@@ -99,20 +101,26 @@ __device__ __forceinline__ void rcp_chunk(const float (&sv)[kChunk], float (&rs)
     }
 }
 
-// Quantize one smoothed value with step d (rd = RN(1/d)); the code is the low
-// byte of the result (code_bits).  In static mode the dividend is first
-// limited to +-128 d (exact scaling by a power of two), which keeps the
-// quotient finite and leaves every code unchanged: a quotient beyond 127.5
-// saturates to +-127 either way.  With a step taken from the row's (or the
-// batch's) own maximum m, d = RN(max(FLOOR, m) / 127) >= m / 127 (1 - 2^-24),
-// so |xh / d| <= 127.00001 and the clamp cannot change a code: it is skipped.
+// Quantize a chunk of eight smoothed values with step d (rd = RN(1/d)); each
+// code is the low byte of its word (chunk_codes: rne(RN(xh / d)), clamped in
+// static mode).  In static mode the dividends are first limited to +-128 d
+// (exact scaling by a power of two), which keeps the quotients finite and
+// leaves every code unchanged: a quotient beyond 127.5 saturates to +-127
+// either way.  With a step taken from the row's (or the batch's) own maximum
+// m, d = RN(max(FLOOR, m) / 127) >= m / 127 (1 - 2^-24), so |xh / d| <=
+// 127.00001 and the clamp cannot change a code: it is skipped.
 template <bool STATIC>
-__device__ __forceinline__ uint32_t quantize(float xh, float d, float rd) {
-    if (STATIC) {
+__device__ __forceinline__ void quantize_chunk(const float (&xh)[kChunk], float d, float rd,
+                                               uint32_t (&q)[kChunk]) {
+    if constexpr (STATIC) {
         const float lim = 128.0f * d;
-        xh = fminf(fmaxf(xh, -lim), lim);
+        float x[kChunk];
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) x[e] = fminf(fmaxf(xh[e], -lim), lim);
+        chunk_codes<true>(x, d, rd, q);
+    } else {
+        chunk_codes<false>(xh, d, rd, q);
     }
-    return code_bits<STATIC>(div_rn(xh, d, rd));
 }
 
 // Whether the static quantizer saturates xh: its rounded quotient (after the
@@ -322,8 +330,7 @@ __global__ __launch_bounds__(MAXT) void act_quant_kernel(
                 const int64_t c = tid + static_cast<int64_t>(i) * nthr;
                 if (c < chunks) {
                     uint32_t q[kChunk];
-#pragma unroll
-                    for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[i][e], d, rd);
+                    quantize_chunk<STATIC>(v[i], d, rd, q);
                     *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8_bits(q);
                 }
             }
@@ -439,8 +446,7 @@ __device__ __forceinline__ void long_rows(const T* __restrict__ x, int64_t M, in
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             uint32_t q[kChunk];
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e) q[e] = quantize<false>(v[i][e], d, rd);
+            quantize_chunk<false>(v[i], d, rd, q);
             const uint2 packed = pack8_bits(q);
             if (ok[i]) gstore8(orow + o[i] * 8u, packed);
             __builtin_amdgcn_sched_barrier(0);
@@ -596,8 +602,7 @@ __global__ __launch_bounds__(NT) void act_quant_multi_kernel(
                 const int64_t c = tid + static_cast<int64_t>(i) * NT;
                 if (c < chunks) {
                     uint32_t q[kChunk];
-#pragma unroll
-                    for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[r][i][e], d, rd);
+                    quantize_chunk<STATIC>(v[r][i], d, rd, q);
                     *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8_bits(q);
                 }
             }
@@ -636,9 +641,10 @@ __global__ __launch_bounds__(NT) void act_quant_static_stream_kernel(
                 float v[kChunk];
                 unpack(raw[u], v);
                 uint32_t q[kChunk];
+                float xh[kChunk];
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e)
-                    q[e] = quantize<true>(div_x<T>(v[e], sv[e], rs[e]), d, rd);
+                for (int e = 0; e < kChunk; ++e) xh[e] = div_x<T>(v[e], sv[e], rs[e]);
+                quantize_chunk<true>(xh, d, rd, q);
                 *reinterpret_cast<uint2*>(xq + (m + u) * K + c * kChunk) = pack8_bits(q);
             }
         }
@@ -849,8 +855,7 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_ln2_kernel(
                 const int64_t c = tid + static_cast<int64_t>(i) * kLnThreads;
                 if (c < chunks) {
                     uint32_t q[kChunk];
-#pragma unroll
-                    for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[r][i][e], d, rd);
+                    quantize_chunk<STATIC>(v[r][i], d, rd, q);
                     *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8_bits(q);
                 }
             }
@@ -964,8 +969,7 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_ln_row_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             uint32_t q[kChunk];
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[i][e], d, rd);
+            quantize_chunk<STATIC>(v[i], d, rd, q);
             const uint2 packed = pack8_bits(q);
             if (t + i * kLnThreads < chunks) gstore8(orow + o[i] * 8u, packed);
             __builtin_amdgcn_sched_barrier(0);
@@ -1045,8 +1049,7 @@ __global__ __launch_bounds__(256) void act_quant_rows_kernel(
             if (live) count_clips(v, d, rd, c, clip_ch, nclip);
         } else if ((STATIC || rowmax == nullptr) && live) {
             uint32_t q[kChunk];
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[e], d, rd);
+            quantize_chunk<STATIC>(v, d, rd, q);
             *reinterpret_cast<uint2*>(xq + m * K + c * kChunk) = pack8_bits(q);
         }
         cur = nxt;
@@ -1152,8 +1155,7 @@ __global__ __launch_bounds__(kLnThreads) void act_quant_stream_kernel(
                 continue;
             }
             uint32_t q[kChunk];
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e) q[e] = quantize<STATIC>(v[e], d, rd);
+            quantize_chunk<STATIC>(v, d, rd, q);
             *reinterpret_cast<uint2*>(xq + m * K + c * kChunk) = pack8_bits(q);
         }
     }

@@ -446,8 +446,7 @@ __global__ __launch_bounds__(MAXT) void weight_quant_kernel(
             const int64_t c = tid + static_cast<int64_t>(i) * nthr;
             if (c < chunks) {
                 uint32_t q[kChunk];
-#pragma unroll
-                for (int e = 0; e < kChunk; ++e) q[e] = code_bits<false>(div_rn(v[i][e], d, rd));
+                chunk_codes<false>(v[i], d, rd, q);
                 *reinterpret_cast<uint2*>(orow + c * kChunk) = pack8_bits(q);
             }
         }
@@ -493,8 +492,10 @@ __global__ __launch_bounds__(256) void weight_quant_stream_kernel(
             load_chunk(row, c, v);
             load_chunk(s, c, sv);
             uint32_t q[kChunk];  // no clamp needed, as in weight_quant_kernel
+            float p[kChunk];
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) q[e] = code_bits<false>(div_rn(v[e] * sv[e], d, rd));
+            for (int e = 0; e < kChunk; ++e) p[e] = v[e] * sv[e];
+            chunk_codes<false>(p, d, rd, q);
             *reinterpret_cast<uint2*>(wq + n * K + c * kChunk) = pack8_bits(q);
         }
     }
@@ -553,8 +554,10 @@ __global__ __launch_bounds__(NT, 2) void weight_quant_recompute_kernel(
                 load_chunk(s, c, sv);
                 unpack(raw[i], v);
                 uint32_t q[kChunk];  // the row's own step: no clamp (weight_quant_kernel)
+                float p[kChunk];
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) q[e] = code_bits<false>(div_rn(v[e] * sv[e], d, rd));
+                for (int e = 0; e < kChunk; ++e) p[e] = v[e] * sv[e];
+                chunk_codes<false>(p, d, rd, q);
                 *reinterpret_cast<uint2*>(wq + n * K + c * kChunk) = pack8_bits(q);
             }
         }
@@ -589,8 +592,10 @@ __global__ __launch_bounds__(NT) void weight_quant_given_stream_kernel(
                 float v[kChunk];
                 unpack(raw[u], v);
                 uint32_t q[kChunk];  // the tensor's step bounds every quotient (no clamp)
+                float p[kChunk];
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) q[e] = code_bits<false>(div_rn(v[e] * sv[e], d, rd));
+                for (int e = 0; e < kChunk; ++e) p[e] = v[e] * sv[e];
+                chunk_codes<false>(p, d, rd, q);
                 *reinterpret_cast<uint2*>(wq + (n + u) * K + c * kChunk) = pack8_bits(q);
             }
         }

@@ -191,6 +191,63 @@ __global__ __launch_bounds__(kThreads) void check_div_kernel(
     report(counts, first_bad, n_bad, n_ieee, key_bad);
 }
 
+// `count` chunks of eight values: chunk_codes (the quantizers' code step)
+// against the code of the IEEE quotient, code_bits<CLAMP>(x / d).  Per chunk
+// an absolute maximum m = 2^(j - 30) (1 + f), j < 60, drawn from (seed, key),
+// with d and RN(1/d) formed as the kernels form them (step_rcp); element e is
+// RN((k + f) d) for an integer k (|k| <= 126; with CLAMP |k| <= 140 and the
+// dividend then limited to +-128 d, as the static quantizer limits it) and a
+// fraction f uniform in [-1/2, 1/2), or, for about half of the elements, the
+// value RN((k + 1/2) d) moved by -4..4 ulps (exact ties and near-ties, where
+// the short form must defer to the division).  raw != 0: the short form
+// without that deferral (the negative control).  Key = chunk index.
+template <bool CLAMP>
+__global__ __launch_bounds__(kThreads) void check_codes_kernel(
+    uint32_t seed, uint32_t count, int raw, unsigned long long* __restrict__ counts,
+    uint32_t* __restrict__ first_bad) {
+    constexpr float kM = 12582912.0f;  // 1.5 * 2^23
+    constexpr int kSpan = CLAMP ? 281 : 253;
+    uint32_t n_bad = 0, key_bad = 0xffffffffu;
+    const uint32_t stride = gridDim.x * kThreads;
+    for (uint32_t key = blockIdx.x * kThreads + threadIdx.x; key < count; key += stride) {
+        const uint32_t h0 = mix32(key ^ mix32(seed));
+        const uint32_t h1 = mix32(h0 ^ 0x68e31da4u);
+        const float m = __uint_as_float(((97u + h0 % 60u) << 23) | (h1 & 0x7fffffu));
+        float d, rd;
+        sq::step_rcp(m, d, rd);
+        const float lim = 128.0f * d;
+        float x[sq::kChunk];
+#pragma unroll
+        for (int e = 0; e < sq::kChunk; ++e) {
+            const uint32_t h = mix32(h1 + 0x9e3779b9u * static_cast<uint32_t>(e + 1));
+            const float k = static_cast<float>(static_cast<int>(h % kSpan) - kSpan / 2);
+            float v;
+            if (h & 0x80000000u) {
+                const float tie = (k + 0.5f) * d;
+                v = __uint_as_float(__float_as_uint(tie) + ((h >> 24) % 9u) - 4u);
+            } else {
+                v = (k + (static_cast<float>((h >> 8) & 0xffffu) * 0x1p-16f - 0.5f)) * d;
+            }
+            x[e] = CLAMP ? fminf(fmaxf(v, -lim), lim) : v;
+        }
+        uint32_t q[sq::kChunk];
+        sq::chunk_codes<CLAMP>(x, d, rd, q);
+#pragma unroll
+        for (int e = 0; e < sq::kChunk; ++e) {
+            uint32_t got = q[e];
+            if (raw) {
+                const float c = __builtin_fmaf(x[e], rd, kM);
+                got = __float_as_uint(CLAMP ? __builtin_amdgcn_fmed3f(c, kM - sq::kQmax, kM + sq::kQmax) : c);
+            }
+            if ((got & 0xffu) != (sq::code_bits<CLAMP>(x[e] / d) & 0xffu)) {
+                ++n_bad;
+                key_bad = min(key_bad, key);
+            }
+        }
+    }
+    report(counts, first_bad, n_bad, 0u, key_bad);
+}
+
 // Elementwise IEEE quotient a[i] / b[i] as the compiler emits it (the
 // library's reference division; the host checks it against its own).
 __global__ __launch_bounds__(kThreads) void div_ref_kernel(const float* __restrict__ a,
@@ -254,6 +311,17 @@ int sqp_check_div(uint32_t seed, uint32_t count, int raw, unsigned long long* co
     if (counts == nullptr || first_bad == nullptr || count == 0) return 1;
     check_div_kernel<<<8192, kThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(
         seed, count, raw, counts, first_bad);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int sqp_check_codes(uint32_t seed, uint32_t count, int clamp, int raw, unsigned long long* counts,
+                    uint32_t* first_bad, sqp_stream_t stream) {
+    if (counts == nullptr || first_bad == nullptr || count == 0) return 1;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (clamp)
+        check_codes_kernel<true><<<8192, kThreads, 0, st>>>(seed, count, raw, counts, first_bad);
+    else
+        check_codes_kernel<false><<<8192, kThreads, 0, st>>>(seed, count, raw, counts, first_bad);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -36,9 +36,10 @@ def lib():
         L.sqp_check_rcp.argtypes = [u32, u32, ci, vp, vp, vp]
         L.sqp_check_div_narrow.argtypes = [ci, vp, vp, vp]
         L.sqp_check_div.argtypes = [u32, u32, ci, vp, vp, vp]
+        L.sqp_check_codes.argtypes = [u32, u32, ci, ci, vp, vp, vp]
         L.sqp_div_ref.argtypes = [vp, vp, vp, i64, vp]
         for f in (L.sqp_mfma_i8, L.sqp_read, L.sqp_copy, L.sqp_check_rcp, L.sqp_check_div_narrow,
-                  L.sqp_check_div, L.sqp_div_ref):
+                  L.sqp_check_div, L.sqp_check_codes, L.sqp_div_ref):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -187,6 +188,14 @@ def check_div(dev, seed: int, count: int, raw: bool = False):
     L = lib()
     return _run_check(dev, lambda c, f, s: _check(L.sqp_check_div(seed, count, int(raw), c, f, s),
                                                   "sqp_check_div"))
+
+
+def check_codes(dev, seed: int, count: int, clamp: bool, raw: bool = False):
+    """The quantizers' code step on `count` hashed chunks of eight values
+    against the codes of the IEEE quotient (sq_probe.h)."""
+    L = lib()
+    return _run_check(dev, lambda c, f, s: _check(
+        L.sqp_check_codes(seed, count, int(clamp), int(raw), c, f, s), "sqp_check_codes"))
 
 
 def div_ref(dev, a, b):
