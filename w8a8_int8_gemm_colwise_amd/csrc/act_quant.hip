@@ -1220,8 +1220,8 @@ hipError_t run_multi(const ActArgs& a, hipStream_t stream) {
     const int64_t pairs = (a.M + 1) / 2;
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     if (chunks <= 512) {
-        // at most the blocks one round holds (72 VGPRs: three blocks of 512
-        // lanes or seven of 256 per CU); the rest take further row pairs
+        // at most the blocks one round holds (77 VGPRs: three blocks of 512
+        // lanes per CU; 73: six of 256); the rest take further row pairs
         // with the next pair in flight.  Measured against 1024 / 2048 blocks,
         // outputs identical, caches flushed: 2048 x 4096 10.7 us vs 11.0,
         // 4096 x 4096 13.9 vs 14.7-15.0, 2048 x 3072 9.8 vs 10.5, 16384 x 2048
